@@ -1,0 +1,244 @@
+// C ABI of the library: argument validation, workspace carve-up and launches on the
+// caller's stream.  Validation mirrors the host launchers on the pages (boostr
+// flash_bwd.rs: shape, contiguity and dtype checks returning InvalidArgument before any
+// launch; rustytorch backward.rs: shape checks and "not on the device" errors), adapted to
+// raw pointers: shapes arrive as integers, so what is checked here is what pointers and
+// sizes can express; the Python binding checks tensor shapes, strides and devices.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/fab.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fab_status fail(fab_status s, const char* arg, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = std::string(arg) + ": " + buf;
+  return s;
+}
+
+bool log_enabled() {
+  static int v = [] {
+    const char* e = getenv("FAB_LOG");
+    return (e && e[0] && e[0] != '0') ? 1 : 0;
+  }();
+  return v != 0;
+}
+
+void log_launch(const fab::LaunchInfo& li) {
+  if (log_enabled())
+    fprintf(stderr, "[fab] %s grid=%d block=%d lds=%d B\n", li.name, li.grid, li.block, li.lds_bytes);
+}
+
+constexpr long long kMaxElems = (1LL << 31) - 1;
+
+size_t elem_size(int dt) { return dt == FAB_F32 ? 4 : 2; }
+
+fab_status check_common(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype) {
+  if (dtype != FAB_F32 && dtype != FAB_F16 && dtype != FAB_BF16)
+    return fail(FAB_ERR_UNSUPPORTED, "dtype", "unsupported dtype code %d (expected 0=f32, 1=f16, 2=bf16)", dtype);
+  if (B < 1 || H < 1 || H_kv < 1 || Sq < 1 || Sk < 1 || D < 1)
+    return fail(FAB_ERR_INVALID_ARGUMENT, "dims",
+                "every size must be >= 1 (B=%d H=%d H_kv=%d Sq=%d Sk=%d D=%d)", B, H, H_kv, Sq, Sk, D);
+  if (D != 64 && D != 128)
+    return fail(FAB_ERR_UNSUPPORTED, "head_dim", "head dim %d not supported (64 or 128)", D);
+  if (H % H_kv != 0)
+    return fail(FAB_ERR_INVALID_ARGUMENT, "num_kv_heads",
+                "num_heads %d is not a multiple of num_kv_heads %d", H, H_kv);
+  if ((long long)B * H * Sq * D > kMaxElems || (long long)B * H_kv * Sk * D > kMaxElems)
+    return fail(FAB_ERR_INVALID_ARGUMENT, "dims", "a tensor exceeds 2^31-1 elements");
+  return FAB_OK;
+}
+
+fab_status check_ptr(const void* p, const char* name) {
+  if (p == nullptr) return fail(FAB_ERR_INVALID_ARGUMENT, name, "null pointer");
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+    return fail(FAB_ERR_INVALID_ARGUMENT, name, "pointer %p is not 16-byte aligned", p);
+  return FAB_OK;
+}
+
+// The pointer must be device memory of the current device whose allocation covers
+// [p, p + bytes).  Run after the cheap checks, so invalid arguments never touch the runtime.
+fab_status check_device_range(const void* p, size_t bytes, const char* name) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(FAB_ERR_DEVICE, name, "no usable GPU (%s)", hipGetErrorString(e));
+  hipPointerAttribute_t attr;
+  e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess || attr.type != hipMemoryTypeDevice) {
+    (void)hipGetLastError();
+    return fail(FAB_ERR_DEVICE, name, "pointer %p is not device memory", p);
+  }
+  if (attr.device != dev)
+    return fail(FAB_ERR_DEVICE, name, "pointer is on device %d, current device is %d", attr.device, dev);
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  e = hipMemGetAddressRange(&base, &size, const_cast<void*>(p));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(FAB_ERR_DEVICE, name, "cannot query the allocation of %p", p);
+  }
+  const char* lo = static_cast<const char*>(base);
+  const char* q = static_cast<const char*>(p);
+  if (q < lo || (size_t)(q - lo) + bytes > size)
+    return fail(FAB_ERR_DEVICE, name, "allocation holds %zu bytes from %p, tensor needs %zu",
+                size - (size_t)(q - lo), p, bytes);
+  return FAB_OK;
+}
+
+size_t ws_bytes(long long B, long long H, long long Sq) {
+  const size_t d = (size_t)(B * H * Sq) * 4;
+  return (d + 255) / 256 * 256;
+}
+
+int units_per_xcd(int n_units) { return n_units % 8 == 0 ? n_units / 8 : 0; }
+
+#define FAB_TRY(x)                    \
+  do {                                \
+    fab_status s_ = (x);              \
+    if (s_ != FAB_OK) return s_;      \
+  } while (0)
+
+fab_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FAB_ERR_LAUNCH, what, "launch failed: %s", hipGetErrorString(e));
+  return FAB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fab_version(void) { return "fab 0.1.0 (gfx950)"; }
+
+const char* fab_last_error(void) { return g_last_error.c_str(); }
+
+size_t fab_bwd_workspace_bytes(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype) {
+  std::string saved = g_last_error;
+  fab_status s = check_common(B, H, H_kv, Sq, Sk, D, dtype);
+  g_last_error = saved;
+  if (s != FAB_OK) return 0;
+  return ws_bytes(B, H, Sq);
+}
+
+fab_status fab_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int H_kv, int Sq, int Sk, int D, int dtype,
+                   int causal, float scale, void* stream) {
+  FAB_TRY(check_common(B, H, H_kv, Sq, Sk, D, dtype));
+  FAB_TRY(check_ptr(q, "q"));
+  FAB_TRY(check_ptr(k, "k"));
+  FAB_TRY(check_ptr(v, "v"));
+  FAB_TRY(check_ptr(o, "o"));
+  FAB_TRY(check_ptr(lse, "lse"));
+  if (!std::isfinite(scale)) return fail(FAB_ERR_INVALID_ARGUMENT, "scale", "scale must be finite");
+  const size_t es = elem_size(dtype);
+  const size_t nq = (size_t)B * H * Sq * D * es, nk = (size_t)B * H_kv * Sk * D * es;
+  FAB_TRY(check_device_range(q, nq, "q"));
+  FAB_TRY(check_device_range(k, nk, "k"));
+  FAB_TRY(check_device_range(v, nk, "v"));
+  FAB_TRY(check_device_range(o, nq, "o"));
+  FAB_TRY(check_device_range(lse, (size_t)B * H * Sq * 4, "lse"));
+
+  fab::FwdParams p;
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.B = B; p.H = H; p.H_kv = H_kv; p.Sq = Sq; p.Sk = Sk;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.scale_log2 = scale * fab::kLog2eHost;
+  p.n_units = B * H_kv;
+  p.units_per_xcd = units_per_xcd(p.n_units);
+  fab::LaunchInfo li;
+  FAB_TRY(launched(fab::launch_fwd(p, dtype, D, (hipStream_t)stream, &li), "fwd"));
+  log_launch(li);
+  return FAB_OK;
+}
+
+fab_status fab_bwd_preprocess(const void* dO, const void* o, float* delta,
+                              int B, int H, int Sq, int D, int dtype, void* stream) {
+  FAB_TRY(check_common(B, H, H, Sq, 1, D, dtype));
+  FAB_TRY(check_ptr(dO, "dO"));
+  FAB_TRY(check_ptr(o, "o"));
+  FAB_TRY(check_ptr(delta, "delta"));
+  const size_t nq = (size_t)B * H * Sq * D * elem_size(dtype);
+  FAB_TRY(check_device_range(dO, nq, "dO"));
+  FAB_TRY(check_device_range(o, nq, "o"));
+  FAB_TRY(check_device_range(delta, (size_t)B * H * Sq * 4, "delta"));
+  fab::PreParams p{dO, o, delta, (long long)B * H * Sq};
+  fab::LaunchInfo li;
+  FAB_TRY(launched(fab::launch_preprocess(p, dtype, D, (hipStream_t)stream, &li), "preprocess"));
+  log_launch(li);
+  return FAB_OK;
+}
+
+fab_status fab_bwd(const void* dO, const void* q, const void* k, const void* v,
+                   const void* o, const float* lse, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes,
+                   int B, int H, int H_kv, int Sq, int Sk, int D, int dtype,
+                   int causal, float scale, void* stream) {
+  FAB_TRY(check_common(B, H, H_kv, Sq, Sk, D, dtype));
+  FAB_TRY(check_ptr(dO, "dO"));
+  FAB_TRY(check_ptr(q, "q"));
+  FAB_TRY(check_ptr(k, "k"));
+  FAB_TRY(check_ptr(v, "v"));
+  FAB_TRY(check_ptr(o, "o"));
+  FAB_TRY(check_ptr(lse, "lse"));
+  FAB_TRY(check_ptr(dq, "dq"));
+  FAB_TRY(check_ptr(dk, "dk"));
+  FAB_TRY(check_ptr(dv, "dv"));
+  FAB_TRY(check_ptr(workspace, "workspace"));
+  if (!std::isfinite(scale)) return fail(FAB_ERR_INVALID_ARGUMENT, "scale", "scale must be finite");
+  const size_t need = ws_bytes(B, H, Sq);
+  if (workspace_bytes < need)
+    return fail(FAB_ERR_INVALID_ARGUMENT, "workspace", "%zu bytes given, %zu needed", workspace_bytes, need);
+  const size_t es = elem_size(dtype);
+  const size_t nq = (size_t)B * H * Sq * D * es, nk = (size_t)B * H_kv * Sk * D * es;
+  const size_t nl = (size_t)B * H * Sq * 4;
+  FAB_TRY(check_device_range(dO, nq, "dO"));
+  FAB_TRY(check_device_range(q, nq, "q"));
+  FAB_TRY(check_device_range(k, nk, "k"));
+  FAB_TRY(check_device_range(v, nk, "v"));
+  FAB_TRY(check_device_range(o, nq, "o"));
+  FAB_TRY(check_device_range(lse, nl, "lse"));
+  FAB_TRY(check_device_range(dq, nq, "dq"));
+  FAB_TRY(check_device_range(dk, nk, "dk"));
+  FAB_TRY(check_device_range(dv, nk, "dv"));
+  FAB_TRY(check_device_range(workspace, need, "workspace"));
+
+  hipStream_t s = (hipStream_t)stream;
+  float* delta = static_cast<float*>(workspace);
+  fab::LaunchInfo li;
+
+  fab::PreParams pp{dO, o, delta, (long long)B * H * Sq};
+  FAB_TRY(launched(fab::launch_preprocess(pp, dtype, D, s, &li), "preprocess"));
+  log_launch(li);
+
+  fab::BwdParams p;
+  p.q = q; p.k = k; p.v = v; p.dO = dO; p.lse = lse; p.delta = delta;
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  p.B = B; p.H = H; p.H_kv = H_kv; p.Sq = Sq; p.Sk = Sk;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.scale_log2 = scale * fab::kLog2eHost;
+  p.n_units = B * H_kv;
+  p.units_per_xcd = units_per_xcd(p.n_units);
+  FAB_TRY(launched(fab::launch_bwd_dkdv(p, dtype, D, s, &li), "bwd_dkdv"));
+  log_launch(li);
+  FAB_TRY(launched(fab::launch_bwd_dq(p, dtype, D, s, &li), "bwd_dq"));
+  log_launch(li);
+  return FAB_OK;
+}
+
+}  // extern "C"

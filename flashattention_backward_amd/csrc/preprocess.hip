@@ -1,0 +1,63 @@
+// Step 1 of the backward (boostr flash_bwd.rs, "Step 1: Preprocessing"):
+//   delta[row] = sum_d dO[row, d] * o[row, d]   (float32), one row per (b, h, query).
+//
+// HBM-bound: each row is read once from each of dO and o.  Lanes load 16 contiguous bytes
+// each, so a wavefront reads whole rows with fully coalesced 16-byte loads; the lanes that
+// share a row reduce their partial sums with cross-lane shuffles.
+#include "common.h"
+#include "launch.h"
+
+namespace fab {
+
+template <class T, int HD>
+__global__ __launch_bounds__(256) void preprocess_kernel(const PreParams p) {
+  constexpr int E = 16 / sizeof(T);          // elements per 16-byte load
+  constexpr int L = HD / E;                  // lanes per row (power of two, <= 64)
+  constexpr int ROWS_PER_PASS = 256 / L;
+  constexpr int PASSES = 4;
+  const int tid = threadIdx.x;
+  const int sub = tid % L;
+  const long long row_base = (long long)blockIdx.x * (ROWS_PER_PASS * PASSES);
+  const T* dO = (const T*)p.dO;
+  const T* o = (const T*)p.o;
+#pragma unroll
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const long long row = row_base + pass * ROWS_PER_PASS + tid / L;
+    float acc = 0.f;
+    if (row < p.rows) {
+      const size_t off = (size_t)row * HD + sub * E;
+      if constexpr (sizeof(T) == 2) {
+        typedef T v8 __attribute__((ext_vector_type(8)));
+        const v8 a = *reinterpret_cast<const v8*>(dO + off);
+        const v8 b = *reinterpret_cast<const v8*>(o + off);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
+      } else {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(dO + off);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(o + off);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc += a[e] * b[e];
+      }
+    }
+#pragma unroll
+    for (int w = L / 2; w > 0; w >>= 1) acc += __shfl_xor(acc, w, L);
+    if (sub == 0 && row < p.rows) p.delta[row] = acc;
+  }
+}
+
+template <class T, int HD>
+static hipError_t go(const PreParams& p, hipStream_t s, LaunchInfo* info) {
+  constexpr int rows_per_block = (256 / (HD / (16 / sizeof(T)))) * 4;
+  const long long grid = (p.rows + rows_per_block - 1) / rows_per_block;
+  if (info) *info = LaunchInfo{"preprocess", (int)grid, 256, 0};
+  hipLaunchKernelGGL((preprocess_kernel<T, HD>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_preprocess(const PreParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info) {
+  if (dt == kBF16) return hd == 64 ? go<bf16, 64>(p, s, info) : go<bf16, 128>(p, s, info);
+  if (dt == kF16) return hd == 64 ? go<f16, 64>(p, s, info) : go<f16, 128>(p, s, info);
+  return hd == 64 ? go<float, 64>(p, s, info) : go<float, 128>(p, s, info);
+}
+
+}  // namespace fab

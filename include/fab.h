@@ -1,0 +1,116 @@
+/*
+ * fab -- FlashAttention-2 backward (and its supporting forward) for AMD MI355X (gfx950).
+ *
+ * C ABI.  Every tensor argument is a plain device pointer to dense, row-major memory; no
+ * PyTorch (or any other framework) type appears here.  The caller owns and allocates all
+ * memory, including the backward workspace; the library never allocates or frees device
+ * memory and keeps no pointer after a call returns.
+ *
+ * Operation (boostr 0.1.0, src/ops/cuda/attention/flash_bwd.rs, doc comment of
+ * flash_attention_bwd_impl): the backward runs in two steps -- a preprocessing step that
+ * forms D = rowsum(dO * O) per query row, then a main step that produces dQ, dK and dV,
+ * recomputing P = exp(scale * Q K^T - LSE) tile by tile instead of storing it.  The
+ * autograd glue on boostr's src/ops/autograd_attention.rs page fixes what the backward
+ * consumes (q, k, v, the forward's output and its lse, and dO) and what the forward
+ * returns (output, lse).
+ *
+ * Layouts (the allocation blocks of flash_bwd.rs and the shape checks of rustytorch's
+ * rtx-flash-metal-attention backward.rs):
+ *   q, o, dO, dQ : [B, H,    Sq, D]   element type `dtype`
+ *   k, v, dK, dV : [B, H_kv, Sk, D]   element type `dtype`
+ *   lse          : [B, H,    Sq]      float32, natural-log log-sum-exp of the scaled scores
+ *   D (delta)    : [B, H,    Sq]      float32
+ * Grouped-query heads: H % H_kv == 0 and query head h uses kv head h / (H / H_kv)
+ * (contiguous groups); dK and dV are the sums over the H / H_kv query heads of a group.
+ * Causal masking is top-left aligned: query row i may attend key j iff j <= i.
+ * Supported: dtype FAB_F32 / FAB_F16 / FAB_BF16 (one dtype shared by all element-typed
+ * tensors of a call), head dim D in {64, 128}.
+ *
+ * Streams: all work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ * the call returns without waiting.  Results are valid for later work on the same stream.
+ *
+ * Errors: every argument is validated before anything is enqueued, so a non-OK status
+ * means nothing was launched and no output was written.  fab_last_error() returns a
+ * thread-local "argument: reason" message for the last non-OK status of the calling
+ * thread.  FAB_ERR_LAUNCH is returned if a launch fails after validation.
+ */
+#ifndef FAB_H
+#define FAB_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FAB_F32 = 0, FAB_F16 = 1, FAB_BF16 = 2 } fab_dtype;
+
+typedef enum {
+  FAB_OK = 0,
+  FAB_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad dims, H % H_kv != 0,
+                                   workspace too small, non-finite scale, size limits */
+  FAB_ERR_UNSUPPORTED = 2,      /* dtype or head dim not supported                    */
+  FAB_ERR_DEVICE = 3,           /* a pointer is not device memory of the current GPU,
+                                   or its allocation is smaller than the tensor       */
+  FAB_ERR_LAUNCH = 4            /* a kernel launch failed (message from the runtime)  */
+} fab_status;
+
+/* Version string of the library. */
+const char* fab_version(void);
+
+/* Thread-local message for the last non-OK status returned on this thread ("" if none). */
+const char* fab_last_error(void);
+
+/*
+ * Bytes of device workspace fab_bwd needs for these sizes (0 if the sizes are invalid).
+ * The workspace holds D = rowsum(dO * O) as float32 [B, H, Sq]; its contents are
+ * undefined on entry and on exit.
+ */
+size_t fab_bwd_workspace_bytes(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype);
+
+/*
+ * Supporting forward (boostr autograd_attention.rs, var_flash_attention: the forward
+ * returns the output and the lse that the backward consumes):
+ *   o   = softmax(scale * q k^T over the allowed keys) v        [B, H, Sq, D], dtype
+ *   lse = natural-log log-sum-exp of the allowed scaled scores  [B, H, Sq],   float32
+ * q, k, v, o, lse: device pointers, 16-byte aligned, not overlapping o/lse.
+ */
+fab_status fab_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int H_kv, int Sq, int Sk, int D, int dtype,
+                   int causal, float scale, void* stream);
+
+/*
+ * Step 1 of the backward on its own (flash_bwd.rs, "Step 1: Preprocessing"):
+ *   delta[b, h, i] = sum_d dO[b, h, i, d] * o[b, h, i, d], accumulated in float32.
+ * dO, o: [B, H, Sq, D] dtype; delta: [B, H, Sq] float32.  Device pointers, 16-byte
+ * aligned.  fab_bwd runs this step itself; it is exported for inspection and timing.
+ */
+fab_status fab_bwd_preprocess(const void* dO, const void* o, float* delta,
+                              int B, int H, int Sq, int D, int dtype, void* stream);
+
+/*
+ * Backward (flash_bwd.rs, flash_attention_bwd_impl; autograd_attention.rs,
+ * FlashAttentionBackward::backward):
+ *   P  = exp(scale * q k^T - lse) on allowed pairs, 0 elsewhere
+ *   dP = dO v^T,   dS = P * (dP - D) with D = rowsum(dO * o)
+ *   dV = sum over the group's query heads of P^T dO
+ *   dK = scale * sum over the group's query heads of dS^T q
+ *   dQ = scale * dS k
+ * Inputs dO, q, o: [B, num_heads, Sq, D]; k, v: [B, num_kv_heads, Sk, D]; lse as produced
+ * by fab_fwd.  Outputs dq [B, num_heads, Sq, D], dk and dv [B, num_kv_heads, Sk, D], all in
+ * `dtype`; they need no initialisation and every element is written (rows a causal mask
+ * never reaches get 0).  workspace: at least fab_bwd_workspace_bytes(...) bytes of device
+ * memory.  All pointers 16-byte aligned; outputs must not overlap inputs or each other.
+ * Deterministic: no atomics, identical inputs give bitwise identical outputs.
+ */
+fab_status fab_bwd(const void* dO, const void* q, const void* k, const void* v,
+                   const void* o, const float* lse, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes,
+                   int B, int num_heads, int num_kv_heads, int Sq, int Sk, int D, int dtype,
+                   int causal, float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FAB_H */

@@ -158,10 +158,16 @@ def _worker(args):
         return group, attention_grads(q, k, v, do, causal, scale, groups=[group])
 
 
+def _serial(args):
+    q, k, v, do, causal, scale, group = args
+    return group, attention_grads(q, k, v, do, causal, scale, groups=[group])
+
+
 def grads_for_groups(q, k, v, do, causal: bool, scale: float, groups, jobs: int = 1):
     """attention_grads over several (b, g) groups, optionally in a process pool.
 
-    Each worker receives only its group's slices and uses one BLAS thread.  Returns
+    With jobs > 1 each worker process receives only its group's slices and uses one BLAS
+    thread; with jobs <= 1 the groups run one after another in this process.  Returns
     {(b, g): result dict with the group's slices: o, lse, delta [G,Sq(,D)], dq [G,Sq,D],
     dk, dv [Sk,D]}.
     """
@@ -174,7 +180,7 @@ def grads_for_groups(q, k, v, do, causal: bool, scale: float, groups, jobs: int 
         tasks.append((q64[b:b + 1, hs], k64[b:b + 1, g:g + 1], v64[b:b + 1, g:g + 1],
                       do64[b:b + 1, hs], causal, scale, (0, 0)))
     if jobs <= 1:
-        outs = [_worker(t)[1] for t in tasks]
+        outs = [_serial(t)[1] for t in tasks]  # one process, BLAS threads as configured
     else:
         import multiprocessing as mp
         ctx = mp.get_context("fork")

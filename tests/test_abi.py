@@ -1,0 +1,108 @@
+"""The C ABI on the CPU: the library loads, exports every symbol include/fab.h declares, and
+rejects invalid arguments before touching the GPU (no device is needed for these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import flashattention_backward_amd as fab
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "fab.h")).read()
+    return sorted(set(re.findall(r"\b(fab_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = fab.lib()
+    names = declared_functions()
+    assert {"fab_fwd", "fab_bwd", "fab_bwd_preprocess", "fab_bwd_workspace_bytes",
+            "fab_last_error", "fab_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert b"gfx950" in L.fab_version()
+
+
+def test_workspace_bytes():
+    L = fab.lib()
+    assert L.fab_bwd_workspace_bytes(2, 32, 8, 4096, 4096, 128, 2) == 2 * 32 * 4096 * 4
+    assert L.fab_bwd_workspace_bytes(1, 1, 1, 3, 5, 64, 0) == 256  # rounded up to 256 B
+    assert L.fab_bwd_workspace_bytes(1, 3, 2, 3, 5, 64, 0) == 0    # H % H_kv != 0
+    assert L.fab_bwd_workspace_bytes(1, 1, 1, 3, 5, 96, 0) == 0    # head dim
+    assert L.fab_bwd_workspace_bytes(1, 1, 1, 3, 5, 64, 9) == 0    # dtype
+
+
+P = 1 << 20  # a fake, 16-byte aligned address: validation must fail before using it
+
+
+def bwd(**kw):
+    a = dict(dO=P, q=P, k=P, v=P, o=P, lse=P, dq=P, dk=P, dv=P, ws=P, ws_bytes=1 << 40,
+             B=1, H=4, H_kv=2, Sq=16, Sk=16, D=64, dtype=2, causal=1, scale=0.125)
+    a.update(kw)
+    L = fab.lib()
+    st = L.fab_bwd(a["dO"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["dq"], a["dk"], a["dv"],
+                   a["ws"], a["ws_bytes"], a["B"], a["H"], a["H_kv"], a["Sq"], a["Sk"], a["D"],
+                   a["dtype"], a["causal"], a["scale"], None)
+    return st, L.fab_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=3), 2, "dtype"),
+    (dict(D=96), 2, "head_dim"),
+    (dict(D=0), 1, "dims"),
+    (dict(B=0), 1, "dims"),
+    (dict(Sq=0), 1, "dims"),
+    (dict(Sk=-1), 1, "dims"),
+    (dict(H=3), 1, "num_kv_heads"),
+    (dict(q=0), 1, "q: null"),
+    (dict(dv=0), 1, "dv: null"),
+    (dict(lse=P + 4), 1, "lse: pointer"),
+    (dict(k=P + 8), 1, "k: pointer"),
+    (dict(ws_bytes=10), 1, "workspace"),
+    (dict(scale=float("inf")), 1, "scale"),
+    (dict(scale=float("nan")), 1, "scale"),
+    (dict(B=4096, Sq=65536, D=128, H=8, H_kv=8), 1, "2^31"),
+])
+def test_bwd_rejects_invalid_arguments(kw, status, needle):
+    st, msg = bwd(**kw)
+    assert st == status, (st, msg)
+    assert needle in msg, msg
+
+
+def test_fwd_and_preprocess_reject_invalid_arguments():
+    L = fab.lib()
+    st = L.fab_fwd(P, P, 0, P, P, 1, 2, 1, 8, 8, 64, 1, 0, 0.1, None)
+    assert st == 1 and "v: null" in L.fab_last_error().decode()
+    st = L.fab_fwd(P, P, P, P, P, 1, 2, 1, 8, 8, 64, 1, 0, float("nan"), None)
+    assert st == 1 and "scale" in L.fab_last_error().decode()
+    st = L.fab_bwd_preprocess(P, P, P + 2, 1, 2, 8, 128, 0, None)
+    assert st == 1 and "delta" in L.fab_last_error().decode()
+    st = L.fab_bwd_preprocess(P, P, P, 1, 2, 8, 32, 0, None)
+    assert st == 2
+
+
+def test_error_message_is_thread_local():
+    import threading
+    L = fab.lib()
+    bwd(dtype=3)
+    seen = {}
+
+    def other():
+        seen["msg"] = L.fab_last_error().decode()
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "dtype" in L.fab_last_error().decode()
+
+
+def test_python_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 2, 8, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        fab.fwd(q, q, q)
+    with pytest.raises(ValueError, match="4-D"):
+        fab.bwd(q, q[0], q, q, q, q[..., 0])

@@ -1,0 +1,105 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, element by element.
+
+Tolerances (per output tensor, over all compared elements): fp32 max|err| <= 1e-4 max|ref|;
+bf16/fp16 max|err| <= 2e-2 max|ref| and relative Frobenius error <= 1e-2.  LSE is float32
+in every dtype and is held to the fp32 bound... relative to max|LSE|.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity_helpers import assert_close, check_end_to_end, run_gpu, say, to_np64
+
+pytestmark = pytest.mark.gpu
+
+# Every named workload at a reduced size that the oracle finishes in seconds but that still
+# spans several tiles in both directions and ends in a ragged tail.
+REDUCED = {
+    "fp32_h2_s128_d64": {},  # already small: the full workload
+    "bf16_causal_h8_s1024_d64": dict(B=1, H=3, H_kv=3, Sq=333, Sk=333),
+    "bf16_causal_h16_s2048_d128": dict(B=1, H=2, H_kv=2, Sq=300, Sk=300),
+    "bf16_gqa4_causal_h32_s4096_d128": dict(B=1, H=8, H_kv=2, Sq=272, Sk=272),
+    "fp16_causal_h16_s16384_d128": dict(B=1, H=2, H_kv=2, Sq=513, Sk=513),
+    "fp16_gqa4_h16_sq512_sk8192_d128": dict(B=2, H=4, H_kv=1, Sq=77, Sk=700),
+}
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_named_workloads_reduced(fab, name):
+    w = workloads.scaled(workloads.get(name), **REDUCED[name])
+    check_end_to_end(fab, w)
+
+
+SHAPES = [
+    # (dtype, B, H, H_kv, Sq, Sk, D, causal)
+    ("bf16", 1, 2, 1, 1, 1, 64, False),
+    ("bf16", 1, 2, 1, 1, 1, 128, True),
+    ("fp16", 1, 1, 1, 5, 3, 64, False),
+    ("bf16", 2, 4, 2, 129, 257, 128, True),    # causal, Sk > Sq: keys past Sq-1 get zero grad
+    ("bf16", 1, 4, 1, 260, 70, 64, True),      # causal, Sq > Sk
+    ("fp16", 1, 8, 8, 200, 200, 128, False),
+    ("fp16", 2, 4, 4, 64, 128, 64, True),      # exact tile multiples
+    ("fp32", 1, 2, 1, 100, 150, 128, True),
+    ("fp32", 2, 2, 2, 65, 33, 64, False),
+    ("bf16", 1, 16, 2, 96, 96, 128, False),    # 8 query heads per kv head
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
+def test_shapes_and_edges(fab, shape):
+    dt, B, H, H_kv, Sq, Sk, D, causal = shape
+    w = workloads.Workload(f"edge_{dt}", dt, B, H, H_kv, Sq, Sk, D, causal, seed=1000 + Sq + 7 * Sk)
+    check_end_to_end(fab, w)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp16", "fp32"])
+def test_isolated_backward(fab, dt):
+    """Diagnostic mode: the GPU backward fed the oracle's O (rounded to the dtype) and LSE."""
+    import torch
+    w = workloads.Workload(f"iso_{dt}", dt, 1, 4, 2, 190, 230, 128, True, seed=77)
+    say(f"[case] isolated backward {dt}")
+    q, k, v, do = workloads.make_inputs(w)
+    o64, lse64 = oracle.attention_forward(q, k, v, w.causal, w.scale)
+    tdt = q.dtype
+    o = torch.from_numpy(o64).to(tdt)
+    lse = torch.from_numpy(lse64).float()
+    ref = oracle.attention_backward(do, q, k, v, o, lse.double(), w.causal, w.scale)
+    dev = torch.device("cuda:0")
+    dq, dk, dv = fab.bwd(do.to(dev), q.to(dev), k.to(dev), v.to(dev), o.to(dev), lse.to(dev),
+                         causal=True, scale=w.scale)
+    delta = fab.bwd_preprocess(do.to(dev), o.to(dev))
+    torch.cuda.synchronize()
+    assert_close("delta", to_np64(delta), ref[3], "fp32" if dt == "fp32" else "bf16")
+    for name, g, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        assert_close(name, to_np64(g), r, dt)
+
+
+def test_deterministic(fab):
+    import torch
+    w = workloads.Workload("det", "bf16", 1, 8, 2, 300, 300, 128, True, seed=5)
+    say("[case] determinism")
+    q, k, v, do = workloads.make_inputs(w)
+    a = run_gpu(fab, q, k, v, do, True, w.scale)
+    b = run_gpu(fab, q, k, v, do, True, w.scale)
+    for key in ("o", "lse", "dq", "dk", "dv"):
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_causal_zero_rows_and_invariants(fab):
+    """Exact zeros where the mask cuts every path; shift and row-stochastic invariants."""
+    import torch
+    w = workloads.Workload("inv", "fp32", 1, 4, 2, 150, 190, 64, True, seed=9)
+    say("[case] invariants")
+    q, k, v, do = workloads.make_inputs(w)
+    out = run_gpu(fab, q, k, v, do, True, w.scale)
+    dk, dv, dq = to_np64(out["dk"]), to_np64(out["dv"]), to_np64(out["dq"])
+    # keys 150..189 are beyond the last query row: no query attends them
+    assert np.all(dk[:, :, 150:] == 0.0) and np.all(dv[:, :, 150:] == 0.0)
+    # the first query row attends only key 0: dq row 0 ~ 0
+    assert np.max(np.abs(dq[:, :, 0])) <= 1e-5 * max(1.0, np.max(np.abs(dq)))
+    # sum_j dK_j = 0 (shift invariance), sum_j dV_j = sum over the group of dO
+    assert np.max(np.abs(dk.sum(axis=2))) <= 1e-4 * np.abs(dk).sum(axis=2).max()
+    do64 = to_np64(do)
+    np.testing.assert_allclose(dv.sum(axis=2), do64.reshape(1, 2, 2, 150, 64).sum(axis=(2, 3)),
+                               rtol=1e-4, atol=1e-4)
