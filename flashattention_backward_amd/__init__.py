@@ -60,6 +60,10 @@ def lib() -> ctypes.CDLL:
             L.fab_bwd_preprocess.argtypes = [vp] * 3 + [i] * 5 + [vp]
             L.fab_bwd.restype = i
             L.fab_bwd.argtypes = [vp] * 10 + [sz] + [i] * 7 + [i, f, vp]
+            L.fab_bwd_dkdv.restype = i
+            L.fab_bwd_dkdv.argtypes = [vp] * 8 + [i] * 7 + [i, f, vp]
+            L.fab_bwd_dq.restype = i
+            L.fab_bwd_dq.argtypes = [vp] * 7 + [i] * 7 + [i, f, vp]
             _lib = L
     return _lib
 

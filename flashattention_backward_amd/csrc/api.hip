@@ -43,6 +43,12 @@ void log_launch(const fab::LaunchInfo& li) {
     fprintf(stderr, "[fab] %s grid=%d block=%d lds=%d B\n", li.name, li.grid, li.block, li.lds_bytes);
 }
 
+#define FAB_TRY(x)                    \
+  do {                                \
+    fab_status s_ = (x);              \
+    if (s_ != FAB_OK) return s_;      \
+  } while (0)
+
 constexpr long long kMaxElems = (1LL << 31) - 1;
 
 size_t elem_size(int dt) { return dt == FAB_F32 ? 4 : 2; }
@@ -107,11 +113,47 @@ size_t ws_bytes(long long B, long long H, long long Sq) {
 
 int units_per_xcd(int n_units) { return n_units % 8 == 0 ? n_units / 8 : 0; }
 
-#define FAB_TRY(x)                    \
-  do {                                \
-    fab_status s_ = (x);              \
-    if (s_ != FAB_OK) return s_;      \
-  } while (0)
+fab::BwdParams bwd_params(const void* dO, const void* q, const void* k, const void* v,
+                          const float* lse, const float* delta, void* dq, void* dk, void* dv,
+                          int B, int H, int H_kv, int Sq, int Sk, int causal, float scale) {
+  fab::BwdParams p;
+  p.q = q; p.k = k; p.v = v; p.dO = dO; p.lse = lse; p.delta = delta;
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  p.B = B; p.H = H; p.H_kv = H_kv; p.Sq = Sq; p.Sk = Sk;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.scale_log2 = scale * fab::kLog2eHost;
+  p.n_units = B * H_kv;
+  p.units_per_xcd = units_per_xcd(p.n_units);
+  return p;
+}
+
+// Checks shared by fab_bwd and the two step-2 entry points (every pointer but dq/dk/dv).
+fab_status check_bwd_inputs(const void* dO, const void* q, const void* k, const void* v,
+                            const float* lse, int B, int H, int H_kv, int Sq, int Sk, int D,
+                            int dtype, float scale) {
+  FAB_TRY(check_common(B, H, H_kv, Sq, Sk, D, dtype));
+  FAB_TRY(check_ptr(dO, "dO"));
+  FAB_TRY(check_ptr(q, "q"));
+  FAB_TRY(check_ptr(k, "k"));
+  FAB_TRY(check_ptr(v, "v"));
+  FAB_TRY(check_ptr(lse, "lse"));
+  if (!std::isfinite(scale)) return fail(FAB_ERR_INVALID_ARGUMENT, "scale", "scale must be finite");
+  return FAB_OK;
+}
+
+fab_status check_bwd_device(const void* dO, const void* q, const void* k, const void* v,
+                            const float* lse, int B, int H, int H_kv, int Sq, int Sk, int D,
+                            int dtype) {
+  const size_t es = elem_size(dtype);
+  const size_t nq = (size_t)B * H * Sq * D * es, nk = (size_t)B * H_kv * Sk * D * es;
+  FAB_TRY(check_device_range(dO, nq, "dO"));
+  FAB_TRY(check_device_range(q, nq, "q"));
+  FAB_TRY(check_device_range(k, nk, "k"));
+  FAB_TRY(check_device_range(v, nk, "v"));
+  FAB_TRY(check_device_range(lse, (size_t)B * H * Sq * 4, "lse"));
+  return FAB_OK;
+}
 
 fab_status launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(FAB_ERR_LAUNCH, what, "launch failed: %s", hipGetErrorString(e));
@@ -188,30 +230,19 @@ fab_status fab_bwd(const void* dO, const void* q, const void* k, const void* v,
                    void* workspace, size_t workspace_bytes,
                    int B, int H, int H_kv, int Sq, int Sk, int D, int dtype,
                    int causal, float scale, void* stream) {
-  FAB_TRY(check_common(B, H, H_kv, Sq, Sk, D, dtype));
-  FAB_TRY(check_ptr(dO, "dO"));
-  FAB_TRY(check_ptr(q, "q"));
-  FAB_TRY(check_ptr(k, "k"));
-  FAB_TRY(check_ptr(v, "v"));
+  FAB_TRY(check_bwd_inputs(dO, q, k, v, lse, B, H, H_kv, Sq, Sk, D, dtype, scale));
   FAB_TRY(check_ptr(o, "o"));
-  FAB_TRY(check_ptr(lse, "lse"));
   FAB_TRY(check_ptr(dq, "dq"));
   FAB_TRY(check_ptr(dk, "dk"));
   FAB_TRY(check_ptr(dv, "dv"));
   FAB_TRY(check_ptr(workspace, "workspace"));
-  if (!std::isfinite(scale)) return fail(FAB_ERR_INVALID_ARGUMENT, "scale", "scale must be finite");
   const size_t need = ws_bytes(B, H, Sq);
   if (workspace_bytes < need)
     return fail(FAB_ERR_INVALID_ARGUMENT, "workspace", "%zu bytes given, %zu needed", workspace_bytes, need);
   const size_t es = elem_size(dtype);
   const size_t nq = (size_t)B * H * Sq * D * es, nk = (size_t)B * H_kv * Sk * D * es;
-  const size_t nl = (size_t)B * H * Sq * 4;
-  FAB_TRY(check_device_range(dO, nq, "dO"));
-  FAB_TRY(check_device_range(q, nq, "q"));
-  FAB_TRY(check_device_range(k, nk, "k"));
-  FAB_TRY(check_device_range(v, nk, "v"));
+  FAB_TRY(check_bwd_device(dO, q, k, v, lse, B, H, H_kv, Sq, Sk, D, dtype));
   FAB_TRY(check_device_range(o, nq, "o"));
-  FAB_TRY(check_device_range(lse, nl, "lse"));
   FAB_TRY(check_device_range(dq, nq, "dq"));
   FAB_TRY(check_device_range(dk, nk, "dk"));
   FAB_TRY(check_device_range(dv, nk, "dv"));
@@ -220,23 +251,51 @@ fab_status fab_bwd(const void* dO, const void* q, const void* k, const void* v,
   hipStream_t s = (hipStream_t)stream;
   float* delta = static_cast<float*>(workspace);
   fab::LaunchInfo li;
-
   fab::PreParams pp{dO, o, delta, (long long)B * H * Sq};
   FAB_TRY(launched(fab::launch_preprocess(pp, dtype, D, s, &li), "preprocess"));
   log_launch(li);
-
-  fab::BwdParams p;
-  p.q = q; p.k = k; p.v = v; p.dO = dO; p.lse = lse; p.delta = delta;
-  p.dq = dq; p.dk = dk; p.dv = dv;
-  p.B = B; p.H = H; p.H_kv = H_kv; p.Sq = Sq; p.Sk = Sk;
-  p.causal = causal ? 1 : 0;
-  p.scale = scale;
-  p.scale_log2 = scale * fab::kLog2eHost;
-  p.n_units = B * H_kv;
-  p.units_per_xcd = units_per_xcd(p.n_units);
+  const fab::BwdParams p = bwd_params(dO, q, k, v, lse, delta, dq, dk, dv, B, H, H_kv, Sq, Sk, causal, scale);
   FAB_TRY(launched(fab::launch_bwd_dkdv(p, dtype, D, s, &li), "bwd_dkdv"));
   log_launch(li);
   FAB_TRY(launched(fab::launch_bwd_dq(p, dtype, D, s, &li), "bwd_dq"));
+  log_launch(li);
+  return FAB_OK;
+}
+
+fab_status fab_bwd_dkdv(const void* dO, const void* q, const void* k, const void* v,
+                        const float* lse, const float* delta, void* dk, void* dv,
+                        int B, int H, int H_kv, int Sq, int Sk, int D,
+                        int dtype, int causal, float scale, void* stream) {
+  FAB_TRY(check_bwd_inputs(dO, q, k, v, lse, B, H, H_kv, Sq, Sk, D, dtype, scale));
+  FAB_TRY(check_ptr(delta, "delta"));
+  FAB_TRY(check_ptr(dk, "dk"));
+  FAB_TRY(check_ptr(dv, "dv"));
+  const size_t nk = (size_t)B * H_kv * Sk * D * elem_size(dtype);
+  FAB_TRY(check_bwd_device(dO, q, k, v, lse, B, H, H_kv, Sq, Sk, D, dtype));
+  FAB_TRY(check_device_range(delta, (size_t)B * H * Sq * 4, "delta"));
+  FAB_TRY(check_device_range(dk, nk, "dk"));
+  FAB_TRY(check_device_range(dv, nk, "dv"));
+  const fab::BwdParams p = bwd_params(dO, q, k, v, lse, delta, nullptr, dk, dv, B, H, H_kv, Sq, Sk, causal, scale);
+  fab::LaunchInfo li;
+  FAB_TRY(launched(fab::launch_bwd_dkdv(p, dtype, D, (hipStream_t)stream, &li), "bwd_dkdv"));
+  log_launch(li);
+  return FAB_OK;
+}
+
+fab_status fab_bwd_dq(const void* dO, const void* q, const void* k, const void* v,
+                      const float* lse, const float* delta, void* dq,
+                      int B, int H, int H_kv, int Sq, int Sk, int D,
+                      int dtype, int causal, float scale, void* stream) {
+  FAB_TRY(check_bwd_inputs(dO, q, k, v, lse, B, H, H_kv, Sq, Sk, D, dtype, scale));
+  FAB_TRY(check_ptr(delta, "delta"));
+  FAB_TRY(check_ptr(dq, "dq"));
+  const size_t nq = (size_t)B * H * Sq * D * elem_size(dtype);
+  FAB_TRY(check_bwd_device(dO, q, k, v, lse, B, H, H_kv, Sq, Sk, D, dtype));
+  FAB_TRY(check_device_range(delta, (size_t)B * H * Sq * 4, "delta"));
+  FAB_TRY(check_device_range(dq, nq, "dq"));
+  const fab::BwdParams p = bwd_params(dO, q, k, v, lse, delta, dq, nullptr, nullptr, B, H, H_kv, Sq, Sk, causal, scale);
+  fab::LaunchInfo li;
+  FAB_TRY(launched(fab::launch_bwd_dq(p, dtype, D, (hipStream_t)stream, &li), "bwd_dq"));
   log_launch(li);
   return FAB_OK;
 }

@@ -109,6 +109,23 @@ fab_status fab_bwd(const void* dO, const void* q, const void* k, const void* v,
                    int B, int num_heads, int num_kv_heads, int Sq, int Sk, int D, int dtype,
                    int causal, float scale, void* stream);
 
+/*
+ * The two kernels of step 2 on their own, for inspection and per-kernel timing; fab_bwd
+ * runs them itself after step 1.  `delta` must hold rowsum(dO * o) as produced by
+ * fab_bwd_preprocess for the same dO and o.  Arguments as for fab_bwd.
+ *   fab_bwd_dkdv writes dk, dv (key-tile outer; each workgroup owns a tile of keys and
+ *                sums over every query head of its kv-head group).
+ *   fab_bwd_dq   writes dq (query-tile outer; recomputes S and dP for its query rows).
+ */
+fab_status fab_bwd_dkdv(const void* dO, const void* q, const void* k, const void* v,
+                        const float* lse, const float* delta, void* dk, void* dv,
+                        int B, int num_heads, int num_kv_heads, int Sq, int Sk, int D,
+                        int dtype, int causal, float scale, void* stream);
+fab_status fab_bwd_dq(const void* dO, const void* q, const void* k, const void* v,
+                      const float* lse, const float* delta, void* dq,
+                      int B, int num_heads, int num_kv_heads, int Sq, int Sk, int D,
+                      int dtype, int causal, float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
