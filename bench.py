@@ -44,7 +44,7 @@ CSRC = os.path.join(ROOT, "flashattention_backward_amd", "csrc")
 
 # Contractions each kernel performs per allowed (b, h, query, key) pair, in units of 2*D FLOPs.
 KERNEL_CONTRACTIONS = {"bwd_dkdv": 4, "bwd_dq": 3}
-KERNEL_SOURCE = {"bwd_dkdv": "bwd_dkdv.hip", "bwd_dq": "bwd_dq.hip", "preprocess": "preprocess.hip"}
+KERNEL_SOURCE = {"bwd_dkdv": "bwd16.hip", "bwd_dq": "bwd16.hip", "preprocess": "preprocess.hip"}
 
 
 def allowed_pairs(w) -> float:
@@ -143,7 +143,6 @@ class Bwd:
         self.code = fab.DTYPE_CODES[str(self.q.dtype).replace("torch.", "")]
         nb = fab.bwd_workspace_bytes(w.B, w.H, w.H_kv, w.Sq, w.Sk, w.D, self.code)
         self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
-        self.delta = self.ws[: w.B * w.H * w.Sq * 4].view(torch.float32)
         self.stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         self.dims = (w.B, w.H, w.H_kv, w.Sq, w.Sk, w.D, self.code, int(w.causal), float(w.scale))
         torch.cuda.synchronize()
@@ -160,17 +159,18 @@ class Bwd:
 
     def preprocess(self):
         w = self.w
-        self._ok(self.L.fab_bwd_preprocess(self.do.data_ptr(), self.o.data_ptr(), self.delta.data_ptr(),
+        self._ok(self.L.fab_bwd_preprocess(self.do.data_ptr(), self.o.data_ptr(), self.lse.data_ptr(),
+                                           self.ws.data_ptr(), self.ws.numel(),
                                            w.B, w.H, w.Sq, w.D, self.code, self.stream))
 
     def dkdv(self):
         self._ok(self.L.fab_bwd_dkdv(self.do.data_ptr(), self.q.data_ptr(), self.k.data_ptr(),
-                                     self.v.data_ptr(), self.lse.data_ptr(), self.delta.data_ptr(),
+                                     self.v.data_ptr(), self.ws.data_ptr(), self.ws.numel(),
                                      self.dk.data_ptr(), self.dv.data_ptr(), *self.dims, self.stream))
 
     def dq_(self):
         self._ok(self.L.fab_bwd_dq(self.do.data_ptr(), self.q.data_ptr(), self.k.data_ptr(),
-                                   self.v.data_ptr(), self.lse.data_ptr(), self.delta.data_ptr(),
+                                   self.v.data_ptr(), self.ws.data_ptr(), self.ws.numel(),
                                    self.dq.data_ptr(), *self.dims, self.stream))
 
 
@@ -222,7 +222,7 @@ def bench_workload(w, steps, warmup, with_cpu, inputs=None):
     kflops = 2.0 * w.D * KERNEL_CONTRACTIONS[dom] * allowed_pairs(w)
     achieved = kflops / (k_ms[dom] * 1e-3) / 1e12
     es = 4 if w.dtype == "fp32" else 2
-    pre_bytes = w.B * w.H * w.Sq * (2 * w.D * es + 4)
+    pre_bytes = w.B * w.H * w.Sq * (2 * w.D * es + 4 + 8)  # read dO, O, LSE; write {LSE', D}
     line = {
         "metric": "attention-backward TFLOP/s (bf16, causal) and % of MI355X dense MFMA peak",
         "value": round(tflops, 2),

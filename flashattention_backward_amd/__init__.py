@@ -57,13 +57,13 @@ def lib() -> ctypes.CDLL:
             L.fab_fwd.restype = i
             L.fab_fwd.argtypes = [vp] * 5 + [i] * 7 + [i, f, vp]
             L.fab_bwd_preprocess.restype = i
-            L.fab_bwd_preprocess.argtypes = [vp] * 3 + [i] * 5 + [vp]
+            L.fab_bwd_preprocess.argtypes = [vp] * 4 + [sz] + [i] * 5 + [vp]
             L.fab_bwd.restype = i
             L.fab_bwd.argtypes = [vp] * 10 + [sz] + [i] * 7 + [i, f, vp]
             L.fab_bwd_dkdv.restype = i
-            L.fab_bwd_dkdv.argtypes = [vp] * 8 + [i] * 7 + [i, f, vp]
+            L.fab_bwd_dkdv.argtypes = [vp] * 5 + [sz] + [vp] * 2 + [i] * 7 + [i, f, vp]
             L.fab_bwd_dq.restype = i
-            L.fab_bwd_dq.argtypes = [vp] * 7 + [i] * 7 + [i, f, vp]
+            L.fab_bwd_dq.argtypes = [vp] * 5 + [sz] + [vp] + [i] * 7 + [i, f, vp]
             _lib = L
     return _lib
 
@@ -126,18 +126,27 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None):
     return o, lse
 
 
-def bwd_preprocess(do, o):
-    """Step 1 alone: delta = rowsum(do * o) as float32 [B, H, Sq]."""
+STATS_ROWS = 64  # the workspace pads each (b, h) to a multiple of this many rows
+
+
+def bwd_preprocess(do, o, lse):
+    """Step 1 alone.  Returns (delta [B, H, Sq] float32 = rowsum(do * o), workspace); the
+    workspace holds the per-row statistics the step-2 kernels read."""
     import torch
     _require(o.dim() == 4, "o", f"must be 4-D, got {tuple(o.shape)}")
     B, H, Sq, D = o.shape
     dev = o.device
     _check_tensor(o, "o", o.shape, o.dtype, dev)
     _check_tensor(do, "dO", o.shape, o.dtype, dev)
-    delta = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
-    _check(lib().fab_bwd_preprocess(do.data_ptr(), o.data_ptr(), delta.data_ptr(),
-                                    B, H, Sq, D, _dtype_code(o), _stream_handle(dev)))
-    return delta
+    _check_tensor(lse, "lse", (B, H, Sq), torch.float32, dev)
+    code = _dtype_code(o)
+    nb = bwd_workspace_bytes(B, H, H, Sq, 1, D, code)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    _check(lib().fab_bwd_preprocess(do.data_ptr(), o.data_ptr(), lse.data_ptr(), ws.data_ptr(), nb,
+                                    B, H, Sq, D, code, _stream_handle(dev)))
+    sq_pad = (Sq + STATS_ROWS - 1) // STATS_ROWS * STATS_ROWS
+    stats = ws[: B * H * sq_pad * 8].view(torch.float32).view(B, H, sq_pad, 2)
+    return stats[:, :, :Sq, 1], ws
 
 
 def bwd(do, q, k, v, o, lse, num_heads: int | None = None, num_kv_heads: int | None = None,

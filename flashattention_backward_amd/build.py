@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfab.so")
-SOURCES = ["api.hip", "preprocess.hip", "bwd_dkdv.hip", "bwd_dq.hip", "fwd.hip"]
+SOURCES = ["api.hip", "preprocess.hip", "bwd_dkdv.hip", "bwd_dq.hip", "bwd16.hip", "fwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 # Packed-fp32 VALU forms are disabled for all device code (see the design notes).

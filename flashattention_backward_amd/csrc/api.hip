@@ -107,19 +107,19 @@ fab_status check_device_range(const void* p, size_t bytes, const char* name) {
 }
 
 size_t ws_bytes(long long B, long long H, long long Sq) {
-  const size_t d = (size_t)(B * H * Sq) * 4;
+  const size_t d = (size_t)(B * H) * fab::stats_rows((int)Sq) * 8;
   return (d + 255) / 256 * 256;
 }
 
 int units_per_xcd(int n_units) { return n_units % 8 == 0 ? n_units / 8 : 0; }
 
 fab::BwdParams bwd_params(const void* dO, const void* q, const void* k, const void* v,
-                          const float* lse, const float* delta, void* dq, void* dk, void* dv,
+                          const void* workspace, void* dq, void* dk, void* dv,
                           int B, int H, int H_kv, int Sq, int Sk, int causal, float scale) {
   fab::BwdParams p;
-  p.q = q; p.k = k; p.v = v; p.dO = dO; p.lse = lse; p.delta = delta;
+  p.q = q; p.k = k; p.v = v; p.dO = dO; p.stats = static_cast<const float*>(workspace);
   p.dq = dq; p.dk = dk; p.dv = dv;
-  p.B = B; p.H = H; p.H_kv = H_kv; p.Sq = Sq; p.Sk = Sk;
+  p.B = B; p.H = H; p.H_kv = H_kv; p.Sq = Sq; p.Sk = Sk; p.Sq_pad = fab::stats_rows(Sq);
   p.causal = causal ? 1 : 0;
   p.scale = scale;
   p.scale_log2 = scale * fab::kLog2eHost;
@@ -130,29 +130,56 @@ fab::BwdParams bwd_params(const void* dO, const void* q, const void* k, const vo
 
 // Checks shared by fab_bwd and the two step-2 entry points (every pointer but dq/dk/dv).
 fab_status check_bwd_inputs(const void* dO, const void* q, const void* k, const void* v,
-                            const float* lse, int B, int H, int H_kv, int Sq, int Sk, int D,
-                            int dtype, float scale) {
+                            int B, int H, int H_kv, int Sq, int Sk, int D, int dtype, float scale) {
   FAB_TRY(check_common(B, H, H_kv, Sq, Sk, D, dtype));
   FAB_TRY(check_ptr(dO, "dO"));
   FAB_TRY(check_ptr(q, "q"));
   FAB_TRY(check_ptr(k, "k"));
   FAB_TRY(check_ptr(v, "v"));
-  FAB_TRY(check_ptr(lse, "lse"));
   if (!std::isfinite(scale)) return fail(FAB_ERR_INVALID_ARGUMENT, "scale", "scale must be finite");
   return FAB_OK;
 }
 
 fab_status check_bwd_device(const void* dO, const void* q, const void* k, const void* v,
-                            const float* lse, int B, int H, int H_kv, int Sq, int Sk, int D,
-                            int dtype) {
+                            int B, int H, int H_kv, int Sq, int Sk, int D, int dtype) {
   const size_t es = elem_size(dtype);
   const size_t nq = (size_t)B * H * Sq * D * es, nk = (size_t)B * H_kv * Sk * D * es;
   FAB_TRY(check_device_range(dO, nq, "dO"));
   FAB_TRY(check_device_range(q, nq, "q"));
   FAB_TRY(check_device_range(k, nk, "k"));
   FAB_TRY(check_device_range(v, nk, "v"));
-  FAB_TRY(check_device_range(lse, (size_t)B * H * Sq * 4, "lse"));
   return FAB_OK;
+}
+
+fab_status check_workspace(const void* ws, size_t given, int B, int H, int Sq) {
+  FAB_TRY(check_ptr(ws, "workspace"));
+  const size_t need = ws_bytes(B, H, Sq);
+  if (given < need)
+    return fail(FAB_ERR_INVALID_ARGUMENT, "workspace", "%zu bytes given, %zu needed", given, need);
+  return FAB_OK;
+}
+
+fab::PreParams pre_params(const void* dO, const void* o, const float* lse, void* ws, int B, int H, int Sq) {
+  fab::PreParams pp;
+  pp.dO = dO; pp.o = o; pp.lse = lse; pp.stats = static_cast<float*>(ws);
+  pp.BH = B * H; pp.Sq = Sq; pp.Sq_pad = fab::stats_rows(Sq);
+  return pp;
+}
+
+hipError_t launch_step2(const fab::BwdParams& p, int dtype, int D, hipStream_t s, bool dkdv, bool dq,
+                        fab::LaunchInfo* li) {
+  hipError_t e = hipSuccess;
+  if (dkdv) {
+    e = dtype == FAB_F32 ? fab::launch_bwd_dkdv(p, dtype, D, s, li) : fab::launch_bwd_dkdv16(p, dtype, D, s, li);
+    if (e != hipSuccess) return e;
+    log_launch(*li);
+  }
+  if (dq) {
+    e = dtype == FAB_F32 ? fab::launch_bwd_dq(p, dtype, D, s, li) : fab::launch_bwd_dq16(p, dtype, D, s, li);
+    if (e != hipSuccess) return e;
+    log_launch(*li);
+  }
+  return e;
 }
 
 fab_status launched(hipError_t e, const char* what) {
@@ -208,19 +235,22 @@ fab_status fab_fwd(const void* q, const void* k, const void* v, void* o, float* 
   return FAB_OK;
 }
 
-fab_status fab_bwd_preprocess(const void* dO, const void* o, float* delta,
+fab_status fab_bwd_preprocess(const void* dO, const void* o, const float* lse,
+                              void* workspace, size_t workspace_bytes,
                               int B, int H, int Sq, int D, int dtype, void* stream) {
   FAB_TRY(check_common(B, H, H, Sq, 1, D, dtype));
   FAB_TRY(check_ptr(dO, "dO"));
   FAB_TRY(check_ptr(o, "o"));
-  FAB_TRY(check_ptr(delta, "delta"));
+  FAB_TRY(check_ptr(lse, "lse"));
+  FAB_TRY(check_workspace(workspace, workspace_bytes, B, H, Sq));
   const size_t nq = (size_t)B * H * Sq * D * elem_size(dtype);
   FAB_TRY(check_device_range(dO, nq, "dO"));
   FAB_TRY(check_device_range(o, nq, "o"));
-  FAB_TRY(check_device_range(delta, (size_t)B * H * Sq * 4, "delta"));
-  fab::PreParams p{dO, o, delta, (long long)B * H * Sq};
+  FAB_TRY(check_device_range(lse, (size_t)B * H * Sq * 4, "lse"));
+  FAB_TRY(check_device_range(workspace, ws_bytes(B, H, Sq), "workspace"));
+  const fab::PreParams pp = pre_params(dO, o, lse, workspace, B, H, Sq);
   fab::LaunchInfo li;
-  FAB_TRY(launched(fab::launch_preprocess(p, dtype, D, (hipStream_t)stream, &li), "preprocess"));
+  FAB_TRY(launched(fab::launch_preprocess(pp, dtype, D, (hipStream_t)stream, &li), "preprocess"));
   log_launch(li);
   return FAB_OK;
 }
@@ -230,73 +260,66 @@ fab_status fab_bwd(const void* dO, const void* q, const void* k, const void* v,
                    void* workspace, size_t workspace_bytes,
                    int B, int H, int H_kv, int Sq, int Sk, int D, int dtype,
                    int causal, float scale, void* stream) {
-  FAB_TRY(check_bwd_inputs(dO, q, k, v, lse, B, H, H_kv, Sq, Sk, D, dtype, scale));
+  FAB_TRY(check_bwd_inputs(dO, q, k, v, B, H, H_kv, Sq, Sk, D, dtype, scale));
   FAB_TRY(check_ptr(o, "o"));
+  FAB_TRY(check_ptr(lse, "lse"));
   FAB_TRY(check_ptr(dq, "dq"));
   FAB_TRY(check_ptr(dk, "dk"));
   FAB_TRY(check_ptr(dv, "dv"));
-  FAB_TRY(check_ptr(workspace, "workspace"));
-  const size_t need = ws_bytes(B, H, Sq);
-  if (workspace_bytes < need)
-    return fail(FAB_ERR_INVALID_ARGUMENT, "workspace", "%zu bytes given, %zu needed", workspace_bytes, need);
+  FAB_TRY(check_workspace(workspace, workspace_bytes, B, H, Sq));
   const size_t es = elem_size(dtype);
   const size_t nq = (size_t)B * H * Sq * D * es, nk = (size_t)B * H_kv * Sk * D * es;
-  FAB_TRY(check_bwd_device(dO, q, k, v, lse, B, H, H_kv, Sq, Sk, D, dtype));
+  FAB_TRY(check_bwd_device(dO, q, k, v, B, H, H_kv, Sq, Sk, D, dtype));
   FAB_TRY(check_device_range(o, nq, "o"));
+  FAB_TRY(check_device_range(lse, (size_t)B * H * Sq * 4, "lse"));
   FAB_TRY(check_device_range(dq, nq, "dq"));
   FAB_TRY(check_device_range(dk, nk, "dk"));
   FAB_TRY(check_device_range(dv, nk, "dv"));
-  FAB_TRY(check_device_range(workspace, need, "workspace"));
+  FAB_TRY(check_device_range(workspace, ws_bytes(B, H, Sq), "workspace"));
 
   hipStream_t s = (hipStream_t)stream;
-  float* delta = static_cast<float*>(workspace);
   fab::LaunchInfo li;
-  fab::PreParams pp{dO, o, delta, (long long)B * H * Sq};
+  const fab::PreParams pp = pre_params(dO, o, lse, workspace, B, H, Sq);
   FAB_TRY(launched(fab::launch_preprocess(pp, dtype, D, s, &li), "preprocess"));
   log_launch(li);
-  const fab::BwdParams p = bwd_params(dO, q, k, v, lse, delta, dq, dk, dv, B, H, H_kv, Sq, Sk, causal, scale);
-  FAB_TRY(launched(fab::launch_bwd_dkdv(p, dtype, D, s, &li), "bwd_dkdv"));
-  log_launch(li);
-  FAB_TRY(launched(fab::launch_bwd_dq(p, dtype, D, s, &li), "bwd_dq"));
-  log_launch(li);
+  const fab::BwdParams p = bwd_params(dO, q, k, v, workspace, dq, dk, dv, B, H, H_kv, Sq, Sk, causal, scale);
+  FAB_TRY(launched(launch_step2(p, dtype, D, s, true, true, &li), "step 2"));
   return FAB_OK;
 }
 
 fab_status fab_bwd_dkdv(const void* dO, const void* q, const void* k, const void* v,
-                        const float* lse, const float* delta, void* dk, void* dv,
+                        const void* workspace, size_t workspace_bytes, void* dk, void* dv,
                         int B, int H, int H_kv, int Sq, int Sk, int D,
                         int dtype, int causal, float scale, void* stream) {
-  FAB_TRY(check_bwd_inputs(dO, q, k, v, lse, B, H, H_kv, Sq, Sk, D, dtype, scale));
-  FAB_TRY(check_ptr(delta, "delta"));
+  FAB_TRY(check_bwd_inputs(dO, q, k, v, B, H, H_kv, Sq, Sk, D, dtype, scale));
   FAB_TRY(check_ptr(dk, "dk"));
   FAB_TRY(check_ptr(dv, "dv"));
+  FAB_TRY(check_workspace(workspace, workspace_bytes, B, H, Sq));
   const size_t nk = (size_t)B * H_kv * Sk * D * elem_size(dtype);
-  FAB_TRY(check_bwd_device(dO, q, k, v, lse, B, H, H_kv, Sq, Sk, D, dtype));
-  FAB_TRY(check_device_range(delta, (size_t)B * H * Sq * 4, "delta"));
+  FAB_TRY(check_bwd_device(dO, q, k, v, B, H, H_kv, Sq, Sk, D, dtype));
+  FAB_TRY(check_device_range(workspace, ws_bytes(B, H, Sq), "workspace"));
   FAB_TRY(check_device_range(dk, nk, "dk"));
   FAB_TRY(check_device_range(dv, nk, "dv"));
-  const fab::BwdParams p = bwd_params(dO, q, k, v, lse, delta, nullptr, dk, dv, B, H, H_kv, Sq, Sk, causal, scale);
+  const fab::BwdParams p = bwd_params(dO, q, k, v, workspace, nullptr, dk, dv, B, H, H_kv, Sq, Sk, causal, scale);
   fab::LaunchInfo li;
-  FAB_TRY(launched(fab::launch_bwd_dkdv(p, dtype, D, (hipStream_t)stream, &li), "bwd_dkdv"));
-  log_launch(li);
+  FAB_TRY(launched(launch_step2(p, dtype, D, (hipStream_t)stream, true, false, &li), "bwd_dkdv"));
   return FAB_OK;
 }
 
 fab_status fab_bwd_dq(const void* dO, const void* q, const void* k, const void* v,
-                      const float* lse, const float* delta, void* dq,
+                      const void* workspace, size_t workspace_bytes, void* dq,
                       int B, int H, int H_kv, int Sq, int Sk, int D,
                       int dtype, int causal, float scale, void* stream) {
-  FAB_TRY(check_bwd_inputs(dO, q, k, v, lse, B, H, H_kv, Sq, Sk, D, dtype, scale));
-  FAB_TRY(check_ptr(delta, "delta"));
+  FAB_TRY(check_bwd_inputs(dO, q, k, v, B, H, H_kv, Sq, Sk, D, dtype, scale));
   FAB_TRY(check_ptr(dq, "dq"));
+  FAB_TRY(check_workspace(workspace, workspace_bytes, B, H, Sq));
   const size_t nq = (size_t)B * H * Sq * D * elem_size(dtype);
-  FAB_TRY(check_bwd_device(dO, q, k, v, lse, B, H, H_kv, Sq, Sk, D, dtype));
-  FAB_TRY(check_device_range(delta, (size_t)B * H * Sq * 4, "delta"));
+  FAB_TRY(check_bwd_device(dO, q, k, v, B, H, H_kv, Sq, Sk, D, dtype));
+  FAB_TRY(check_device_range(workspace, ws_bytes(B, H, Sq), "workspace"));
   FAB_TRY(check_device_range(dq, nq, "dq"));
-  const fab::BwdParams p = bwd_params(dO, q, k, v, lse, delta, dq, nullptr, nullptr, B, H, H_kv, Sq, Sk, causal, scale);
+  const fab::BwdParams p = bwd_params(dO, q, k, v, workspace, dq, nullptr, nullptr, B, H, H_kv, Sq, Sk, causal, scale);
   fab::LaunchInfo li;
-  FAB_TRY(launched(fab::launch_bwd_dq(p, dtype, D, (hipStream_t)stream, &li), "bwd_dq"));
-  log_launch(li);
+  FAB_TRY(launched(launch_step2(p, dtype, D, (hipStream_t)stream, false, true, &li), "bwd_dq"));
   return FAB_OK;
 }
 

@@ -1,0 +1,469 @@
+// The two step-2 kernels for 16-bit inputs (bf16, fp16), tiled for gfx950.
+//
+// Both kernels stage their streamed operand tiles with direct global->LDS loads
+// (global_load_lds_dwordx4) into a double buffer, so the next tile arrives while the current
+// one is consumed and each step needs one barrier.  Tiles are row-major and XOR-swizzled
+// (swz in common.h); operands that contract over rows are read with the LDS transpose read
+// (lds_frag_tr) instead of keeping a transposed copy.  Rows past the end of a sequence are
+// loaded from the last valid row (finite data) and neutralised by the masks and by the
+// per-row statistics the preprocess writes for padding rows (LSE = +inf, D = 0).
+//
+// Per-row statistics: stats[(b*H + h) * Sq_pad + i] = {LSE * log2(e), D} with
+// Sq_pad = Sq rounded up to 64 (written by the preprocess kernel).
+#include "common.h"
+#include "launch.h"
+
+namespace fab {
+
+// =======================================================================================
+// dK, dV: key-tile outer (boostr flash_bwd.rs "Step 2": one workgroup per tile of keys).
+// A workgroup owns BN = 128 keys of one (batch, kv head) and walks every query head of the
+// group and every 64-row query tile the causal mask lets reach its keys.  Its 4 waves form a
+// 2 x 2 grid: wave (kb, qh) owns keys [64 kb, 64 kb + 64) and the query rows [32 qh, 32 qh + 32)
+// of each tile, so every Q / dO element read from LDS feeds 64 keys.  K fragments stay in
+// registers, V sits in LDS for the workgroup's life; dK and dV accumulate in registers and
+// the two query halves are summed through LDS at the end.
+// =======================================================================================
+template <int HD>
+struct Dkdv16 {
+  static constexpr int BN = 128, BM = 64;
+  static constexpr int RB = 2 * HD;            // bytes per tile row
+  static constexpr int GPR = RB / 16;          // 16-byte granules per row
+  static constexpr int TILE = BM * RB;         // one Q or dO tile
+  static constexpr int STATS = BM * 8;         // {lse2, D} per row
+  static constexpr int BUF = 2 * TILE + STATS; // one stage: Q, dO, stats
+  static constexpr int VT = BN * RB;           // V tile of the workgroup
+  static constexpr int LDS = 2 * BUF + VT;
+  static constexpr int RED = 2 * 64 * HD * 4;  // epilogue: two waves' partial dK or dV
+  static_assert(RED <= LDS, "reduction must fit in the staging buffers");
+  static constexpr int QI = TILE / 1024;       // direct-load instructions per Q tile
+  static_assert(QI % 4 == 0, "tile loads split evenly over 4 waves");
+};
+
+template <class T, int HD>
+__global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
+  typedef Dkdv16<HD> C;
+  typedef typename Frag<T>::type F;
+  constexpr int NC = HD / 16, NDB = HD / 32;
+  constexpr int BM = C::BM, BN = C::BN, RB = C::RB;
+
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+  char* const vtile = smem + 2 * C::BUF;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
+  const int lane = tid & 63, hl = lane >> 5, c32 = lane & 31;
+  const int kb = w & 1, qh = w >> 1;
+
+  const WorkItem wi = map_work(blockIdx.x, p.n_units, p.units_per_xcd);
+  const int b = wi.unit / p.H_kv, g = wi.unit % p.H_kv;
+  const int n0 = wi.step * BN;
+  const int G = p.H / p.H_kv;
+  const int Sq = p.Sq, Sk = p.Sk, Sq_pad = p.Sq_pad;
+  const bool causal = p.causal != 0;
+  const size_t kv_off = (size_t)(b * p.H_kv + g) * Sk * HD;
+  const T* Kg = (const T*)p.k + kv_off;
+  const T* Vg = (const T*)p.v + kv_off;
+
+  // ---- V tile -> LDS (once), K fragments -> registers (once)
+  {
+    constexpr int VI = C::VT / 1024;  // instructions for the V tile
+    for (int q = w; q < VI; q += 4) {
+      const int gi = 64 * q + lane;
+      const int r = gi / C::GPR, pc = gi % C::GPR;
+      const int n = min(n0 + r, Sk - 1);
+      g2lds16(Vg + (size_t)n * HD + 8 * (pc ^ swz<HD>(r)), vtile + 1024 * q);
+    }
+  }
+  const int nw0 = n0 + 64 * kb;
+  F kf[2][NC];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int n = min(nw0 + 32 * nb + c32, Sk - 1);
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) kf[nb][cc] = ld8(Kg + (size_t)n * HD + 16 * cc + 8 * hl);
+  }
+
+  f32x16 dk[2][NDB], dv[2][NDB];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      dk[nb][db] = f32x16{};
+      dv[nb][db] = f32x16{};
+    }
+
+  // ---- per-lane LDS offsets
+  // A operand (Q or dO rows): row 32 qh + c32, chunk 2 cc + hl
+  int a_off[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) a_off[cc] = swz_off<HD>(32 * qh + c32, 2 * cc + hl);
+  // B operand of P^T dO / dS^T Q, transposed read: 16-lane group (hl, dh), lane i in group
+  const int gi16 = lane & 15, dh = (lane >> 4) & 1;
+  int t_off[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) {
+      const int r = 32 * qh + 4 * hl + 8 * sec + (gi16 >> 2);
+      const int col = 32 * db + 16 * dh + 4 * (gi16 & 3);
+      t_off[db][sec] = swz_off<HD>(r, col >> 3) + 2 * (col & 7);
+    }
+  // B operand of dP = dO V^T: V rows 64 kb + 32 nb + c32 have the same swizzle as the A
+  // operand rows 32 qh + c32 (both are c32 mod 16), so they are a_off plus a wave constant.
+  const char* const vrows = vtile + (64 * kb - 32 * qh) * RB;
+
+  // ---- iteration space: (query head in group, query tile), flattened
+  const int n_qt = (Sq + BM - 1) / BM;
+  const int i_first = causal ? min(n0 / BM, n_qt) : 0;
+  const int per = n_qt - i_first;
+  const int total = G * per;
+
+  auto issue = [&](int s, char* buf) {
+    const int hh = s / per, it = i_first + s % per;
+    const int hq = g * G + hh, m0 = it * BM;
+    const size_t q_off = (size_t)(b * p.H + hq) * Sq;
+    const T* Qg = (const T*)p.q + q_off * HD;
+    const T* dOg = (const T*)p.dO + q_off * HD;
+#pragma unroll
+    for (int k = 0; k < C::QI / 4; ++k) {
+      const int q = w + 4 * k;
+      const int gi = 64 * q + lane;
+      const int r = gi / C::GPR, pc = gi % C::GPR;
+      const size_t src = (size_t)min(m0 + r, Sq - 1) * HD + 8 * (pc ^ swz<HD>(r));
+      g2lds16(Qg + src, buf + 1024 * q);
+      g2lds16(dOg + src, buf + C::TILE + 1024 * q);
+    }
+    if (w == 0 && lane < C::STATS / 16) {
+      const float* st = p.stats + ((size_t)(b * p.H + hq) * Sq_pad + m0) * 2;
+      g2lds16(st + 4 * lane, buf + 2 * C::TILE);
+    }
+  };
+
+  if (total > 0) issue(0, smem);
+  wait_vm_all();
+  __syncthreads();
+
+  for (int s = 0; s < total; ++s) {
+    char* cur = smem + (s & 1) * C::BUF;
+    if (s + 1 < total) issue(s + 1, smem + ((s + 1) & 1) * C::BUF);
+
+    const int it = i_first + s % per;
+    const int m0 = it * BM;
+    const int mw0 = m0 + 32 * qh;
+    // Every wave computes every step (a wave whose keys all lie after its rows gets P = 0
+    // from the mask): the workgroup waits for its slowest wave at the barrier anyway, and
+    // branch-free accumulation keeps the accumulators in place.
+    {
+      f32x16 S[2], dP[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        S[nb] = f32x16{};
+        dP[nb] = f32x16{};
+      }
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        const F aq = lds_frag<T>(cur, a_off[cc]);
+        const F ad = lds_frag<T>(cur + C::TILE, a_off[cc]);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          mma(S[nb], aq, kf[nb][cc]);
+          mma(dP[nb], ad, lds_frag<T>(vrows + 32 * nb * RB, a_off[cc]));
+        }
+      }
+
+      const bool need_mask = (n0 + BN > Sk) || (causal && nw0 + 63 > mw0);
+      const float* st = reinterpret_cast<const float*>(cur + 2 * C::TILE);
+      // P and dS go straight into the 16-bit operand fragments of the next contractions:
+      // fragment (nb, ks) holds accumulator registers 8 ks .. 8 ks + 7 of block nb.
+      F pa[2][2], da[2][2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ml = 32 * qh + 8 * j + 4 * hl;  // first of 4 consecutive rows
+        const f32x4 s01 = *reinterpret_cast<const f32x4*>(st + 2 * ml);
+        const f32x4 s23 = *reinterpret_cast<const f32x4*>(st + 2 * ml + 4);
+        const float l2[4] = {s01[0], s01[2], s23[0], s23[2]};
+        const float dl[4] = {s01[1], s01[3], s23[1], s23[3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * j + e;
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            float pv = fast_exp2(S[nb][r] * p.scale_log2 - l2[e]);
+            if (need_mask) {
+              const int n = nw0 + 32 * nb + c32;
+              const bool cut = (n >= Sk) | (causal & (n > m0 + ml + e));
+              pv = cut ? 0.f : pv;
+            }
+            pa[nb][r >> 3][r & 7] = (T)pv;
+            da[nb][r >> 3][r & 7] = (T)(pv * (dP[nb][r] - dl[e]));
+          }
+        }
+      }
+
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int o_lo = t_off[db][0] + ks * 16 * RB, o_hi = t_off[db][1] + ks * 16 * RB;
+          const F bo = lds_frag_tr<T>(cur + C::TILE, o_lo, o_hi);
+          const F bq = lds_frag_tr<T>(cur, o_lo, o_hi);
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            mma(dv[nb][db], pa[nb][ks], bo);
+            mma(dk[nb][db], da[nb][ks], bq);
+          }
+        }
+      }
+    }
+    wait_vm_all();
+    __syncthreads();
+  }
+
+  // ---- epilogue: the qh = 1 waves hand their partial sums to the qh = 0 waves via LDS,
+  // which add, scale and store.  The accumulators of a wave pair have identical layouts, so
+  // the exchange is lane-major and conflict free.
+  float* red = reinterpret_cast<float*>(smem) + kb * (64 * HD);
+  T* dKg = (T*)p.dk + kv_off;
+  T* dVg = (T*)p.dv + kv_off;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    if (qh == 1) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x16& a = pass == 0 ? dk[nb][db] : dv[nb][db];
+            const int slot = (nb * NDB + db) * 4 + r4;
+            *reinterpret_cast<f32x4*>(red + (slot * 64 + lane) * 4) =
+                f32x4{a[4 * r4], a[4 * r4 + 1], a[4 * r4 + 2], a[4 * r4 + 3]};
+          }
+    }
+    __syncthreads();
+    if (qh == 0) {
+      T* dst = pass == 0 ? dKg : dVg;
+      const float sc = pass == 0 ? p.scale : 1.f;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x16& a = pass == 0 ? dk[nb][db] : dv[nb][db];
+            const int slot = (nb * NDB + db) * 4 + r4;
+            const f32x4 o = *reinterpret_cast<const f32x4*>(red + (slot * 64 + lane) * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int n = nw0 + 32 * nb + 8 * r4 + 4 * hl + e;
+              if (n < Sk) dst[(size_t)n * HD + 32 * db + c32] = (T)((a[4 * r4 + e] + o[e]) * sc);
+            }
+          }
+    }
+    __syncthreads();
+  }
+}
+
+// =======================================================================================
+// dQ: query-tile outer.  A workgroup owns BM = 256 query rows of one (batch, head); wave w
+// owns rows [64 w, 64 w + 64) (two 32-row blocks) with their Q and dO fragments, LSE and D in
+// registers.  Per step of BN = 32 keys it recomputes S^T = K Q^T and dP^T = V dO^T (one query
+// row per lane), forms dS^T = P^T (dP^T - D) and adds dS K into the dQ accumulators.  K and V
+// tiles stream through a double-buffered LDS stage.
+// =======================================================================================
+template <int HD>
+struct Dq16 {
+  static constexpr int BM = 256, BN = 32;
+  static constexpr int RB = 2 * HD;
+  static constexpr int GPR = RB / 16;
+  static constexpr int TILE = BN * RB;    // one K or V tile
+  static constexpr int BUF = 2 * TILE;
+  static constexpr int LDS = 2 * BUF;
+  static constexpr int KI = TILE / 1024;  // direct-load instructions per tile
+};
+
+template <class T, int HD>
+__global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
+  typedef Dq16<HD> C;
+  typedef typename Frag<T>::type F;
+  constexpr int NC = HD / 16, NDB = HD / 32;
+  constexpr int BM = C::BM, BN = C::BN, RB = C::RB;
+
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
+  const int lane = tid & 63, hl = lane >> 5, c32 = lane & 31;
+  const int Sq = p.Sq, Sk = p.Sk;
+  const bool causal = p.causal != 0;
+  const int G = p.H / p.H_kv;
+  const int n_qt = (Sq + BM - 1) / BM;
+
+  const WorkItem wi = map_work(blockIdx.x, p.n_units, p.units_per_xcd);
+  const int b = wi.unit / p.H_kv, g = wi.unit % p.H_kv;
+  const int hq = g * G + wi.step % G;
+  const int tq = wi.step / G;
+  const int it = causal ? n_qt - 1 - tq : tq;
+  const int m0 = it * BM;
+  const int mw0 = m0 + 64 * w;
+
+  const size_t q_off = (size_t)(b * p.H + hq) * Sq;
+  const size_t kv_off = (size_t)(b * p.H_kv + g) * Sk * HD;
+  const T* Qg = (const T*)p.q + q_off * HD;
+  const T* dOg = (const T*)p.dO + q_off * HD;
+  const T* Kg = (const T*)p.k + kv_off;
+  const T* Vg = (const T*)p.v + kv_off;
+
+  F qf[2][NC], dof[2][NC];
+  float lse2[2], dl[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int m = mw0 + 32 * mb + c32;
+    const int mc = min(m, Sq - 1);
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      qf[mb][cc] = ld8(Qg + (size_t)mc * HD + 16 * cc + 8 * hl);
+      dof[mb][cc] = ld8(dOg + (size_t)mc * HD + 16 * cc + 8 * hl);
+    }
+    const float* st = p.stats + ((size_t)(b * p.H + hq) * p.Sq_pad + mc) * 2;
+    lse2[mb] = m < Sq ? st[0] : __builtin_inff();
+    dl[mb] = m < Sq ? st[1] : 0.f;
+  }
+
+  f32x16 dq[2][NDB];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dq[mb][db] = f32x16{};
+
+  int a_off[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) a_off[cc] = swz_off<HD>(c32, 2 * cc + hl);
+  const int gi16 = lane & 15, dh = (lane >> 4) & 1;
+  int t_off[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) {
+      const int r = 4 * hl + 8 * sec + (gi16 >> 2);
+      const int col = 32 * db + 16 * dh + 4 * (gi16 & 3);
+      t_off[db][sec] = swz_off<HD>(r, col >> 3) + 2 * (col & 7);
+    }
+
+  const int n_kt = (Sk + BN - 1) / BN;
+  const int j_end = causal ? min(n_kt, (min(m0 + BM, Sq) - 1) / BN + 1) : n_kt;
+
+  auto issue = [&](int j, char* buf) {
+    const int n0 = j * BN;
+#pragma unroll
+    for (int k = 0; k < (2 * C::KI + 3) / 4; ++k) {
+      const int q = w + 4 * k;  // 0..KI-1: K tile, KI..2KI-1: V tile
+      if (q < 2 * C::KI) {
+        const int tq2 = q < C::KI ? q : q - C::KI;
+        const int gi = 64 * tq2 + lane;
+        const int r = gi / C::GPR, pc = gi % C::GPR;
+        const size_t src = (size_t)min(n0 + r, Sk - 1) * HD + 8 * (pc ^ swz<HD>(r));
+        g2lds16((q < C::KI ? Kg : Vg) + src, buf + 1024 * q);
+      }
+    }
+  };
+
+  if (j_end > 0) issue(0, smem);
+  wait_vm_all();
+  __syncthreads();
+
+  for (int j = 0; j < j_end; ++j) {
+    char* cur = smem + (j & 1) * C::BUF;
+    if (j + 1 < j_end) issue(j + 1, smem + ((j + 1) & 1) * C::BUF);
+    const int n0 = j * BN;
+    {
+      f32x16 St[2], dPt[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        St[mb] = f32x16{};
+        dPt[mb] = f32x16{};
+      }
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        const F ak = lds_frag<T>(cur, a_off[cc]);
+        const F av = lds_frag<T>(cur + C::TILE, a_off[cc]);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          mma(St[mb], ak, qf[mb][cc]);
+          mma(dPt[mb], av, dof[mb][cc]);
+        }
+      }
+      const bool need_mask = (n0 + BN > Sk) || (causal && n0 + BN - 1 > mw0);
+      F da[2][2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int m = mw0 + 32 * mb + c32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pv = fast_exp2(St[mb][r] * p.scale_log2 - lse2[mb]);
+          if (need_mask) {
+            const int n = n0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            const bool cut = (n >= Sk) | (causal & (n > m));
+            pv = cut ? 0.f : pv;
+          }
+          da[mb][r >> 3][r & 7] = (T)(pv * (dPt[mb][r] - dl[mb]));
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const F bk = lds_frag_tr<T>(cur, t_off[db][0] + ks * 16 * RB, t_off[db][1] + ks * 16 * RB);
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) mma(dq[mb][db], da[mb][ks], bk);
+        }
+      }
+    }
+    wait_vm_all();
+    __syncthreads();
+  }
+
+  T* dQg = (T*)p.dq + q_off * HD;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = mw0 + 32 * mb + 8 * (r >> 2) + 4 * hl + (r & 3);
+        if (m < Sq) dQg[(size_t)m * HD + 32 * db + c32] = (T)(dq[mb][db][r] * p.scale);
+      }
+}
+
+template <class T, int HD>
+static hipError_t go_dkdv(const BwdParams& p, hipStream_t s, LaunchInfo* info) {
+  typedef Dkdv16<HD> C;
+  const int n_kt = (p.Sk + C::BN - 1) / C::BN;
+  const int grid = p.n_units * n_kt;
+  if (info) *info = LaunchInfo{"bwd_dkdv16", grid, 256, C::LDS};
+  hipLaunchKernelGGL((bwd_dkdv16_kernel<T, HD>), dim3(grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <class T, int HD>
+static hipError_t go_dq(const BwdParams& p, hipStream_t s, LaunchInfo* info) {
+  typedef Dq16<HD> C;
+  const int n_qt = (p.Sq + C::BM - 1) / C::BM;
+  const int grid = p.n_units * (p.H / p.H_kv) * n_qt;
+  if (info) *info = LaunchInfo{"bwd_dq16", grid, 256, C::LDS};
+  hipLaunchKernelGGL((bwd_dq16_kernel<T, HD>), dim3(grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv16(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info) {
+  if (dt == kBF16) return hd == 64 ? go_dkdv<bf16, 64>(p, s, info) : go_dkdv<bf16, 128>(p, s, info);
+  return hd == 64 ? go_dkdv<f16, 64>(p, s, info) : go_dkdv<f16, 128>(p, s, info);
+}
+
+hipError_t launch_bwd_dq16(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info) {
+  if (dt == kBF16) return hd == 64 ? go_dq<bf16, 64>(p, s, info) : go_dq<bf16, 128>(p, s, info);
+  return hd == 64 ? go_dq<f16, 64>(p, s, info) : go_dq<f16, 128>(p, s, info);
+}
+
+}  // namespace fab

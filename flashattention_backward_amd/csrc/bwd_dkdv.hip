@@ -97,8 +97,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p) {
     const size_t q_off = (size_t)(b * p.H + hq) * Sq;
     const T* Qg = (const T*)p.q + q_off * HD;
     const T* dOg = (const T*)p.dO + q_off * HD;
-    const float* Lg = p.lse + q_off;
-    const float* Dg = p.delta + q_off;
+    const float* Stg = p.stats + (size_t)(b * p.H + hq) * p.Sq_pad * 2;
 
     for (int it = i_first; it < n_qt; ++it) {
       const int m0 = it * BM;
@@ -127,8 +126,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p) {
         }
         for (int t = tid; t < BM; t += 256) {
           const int m = m0 + t;
-          sL[t] = m < Sq ? Lg[m] * kLog2e : __builtin_inff();
-          sD[t] = m < Sq ? Dg[m] : 0.f;
+          sL[t] = m < Sq ? Stg[2 * m] : __builtin_inff();
+          sD[t] = m < Sq ? Stg[2 * m + 1] : 0.f;
         }
       }
       __syncthreads();

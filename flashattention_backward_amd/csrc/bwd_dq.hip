@@ -78,8 +78,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
       dof[c] = zero8<T>();
     }
   }
-  const float lse2 = m < Sq ? p.lse[q_off + m] * kLog2e : __builtin_inff();
-  const float dl = m < Sq ? p.delta[q_off + m] : 0.f;
+  const float* Stg = p.stats + (size_t)(b * p.H + hq) * p.Sq_pad * 2;
+  const float lse2 = m < Sq ? Stg[2 * m] : __builtin_inff();
+  const float dl = m < Sq ? Stg[2 * m + 1] : 0.f;
 
   f32x16 dq[NDB];
 #pragma unroll

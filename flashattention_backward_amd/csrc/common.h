@@ -112,6 +112,52 @@ __device__ __forceinline__ int perm16(int m) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------------------------------
+// Swizzled 16-bit tiles in LDS.  A tile row holds HD elements (2*HD bytes, no padding); the
+// 16-byte chunk c of row r is stored at chunk position c ^ swz<HD>(r).  The XOR pattern is
+// chosen so that both access shapes the kernels use are free of bank conflicts on gfx950
+// (measured): a b128 read of one chunk from 32 consecutive rows, and a ds_read_b64_tr_b16
+// of a 4-row x 16-column block by each 16-lane group.
+template <int HD>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (HD == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+  else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+template <int HD>
+__device__ __forceinline__ int swz_off(int r, int c) {
+  return r * (2 * HD) + 16 * (c ^ swz<HD>(r));
+}
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+template <class T>
+__device__ __forceinline__ typename Frag<T>::type lds_frag(const char* base, int byte_off) {
+  return *reinterpret_cast<const typename Frag<T>::type*>(base + byte_off);
+}
+
+// Transposed fragment from a row-major 16-bit tile: two ds_read_b64_tr_b16.  In each 16-lane
+// group, source lane i addresses 4 consecutive elements of row (row0 + i / 4) starting at
+// column (col0 + 4 * (i % 4)); the result gives group lane i the four rows row0..row0+3 of
+// column col0 + i.  The two reads cover rows row0..+3 and row0+8..+11 (the permuted row order
+// of an accumulator-sourced operand, see perm16).
+template <class T>
+__device__ __forceinline__ typename Frag<T>::type lds_frag_tr(const char* base, int off_lo, int off_hi) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(const lds_char*)(base + off_lo));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(const lds_char*)(base + off_hi));
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(typename Frag<T>::type, v);
+}
+
+// 16 bytes from global memory straight into LDS (global_load_lds_dwordx4): lane l of the wave
+// writes lds_wave_base + 16 * l.  lds_wave_base must be the same for the whole wave.
+__device__ __forceinline__ void g2lds16(const void* src, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_char*)lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Work-item mapping shared by the launches: workgroup ids are dispatched round-robin over
 // the 8 XCDs, so id w runs on XCD w % 8.  When the independent units (kv-head groups) split
 // evenly over the XCDs, give each XCD whole units so that their tiles share its L2; the

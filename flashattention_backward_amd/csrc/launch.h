@@ -9,11 +9,18 @@ enum Dt { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
 constexpr float kLog2eHost = 1.4426950408889634f;
 
+// Per-row statistics the backward kernels consume, written by the preprocess:
+// stats[(b*H + h) * Sq_pad + i] = {LSE[b,h,i] * log2(e), D[b,h,i]}, Sq_pad = Sq rounded up to
+// kStatsRows; padding rows hold {+inf, 0} so that they contribute nothing.
+constexpr int kStatsRows = 64;
+inline int stats_rows(int Sq) { return (Sq + kStatsRows - 1) / kStatsRows * kStatsRows; }
+
 struct PreParams {
   const void* dO;
   const void* o;
-  float* delta;
-  long long rows;  // B * H * Sq
+  const float* lse;
+  float* stats;
+  int BH, Sq, Sq_pad;
 };
 
 struct FwdParams {
@@ -35,12 +42,11 @@ struct BwdParams {
   const void* k;
   const void* v;
   const void* dO;
-  const float* lse;
-  const float* delta;
+  const float* stats;  // see PreParams
   void* dq;
   void* dk;
   void* dv;
-  int B, H, H_kv, Sq, Sk;
+  int B, H, H_kv, Sq, Sk, Sq_pad;
   int causal;
   float scale;
   float scale_log2;
@@ -57,5 +63,7 @@ hipError_t launch_preprocess(const PreParams& p, int dt, int hd, hipStream_t s, 
 hipError_t launch_fwd(const FwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info);
 hipError_t launch_bwd_dkdv(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info);
 hipError_t launch_bwd_dq(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info);
+hipError_t launch_bwd_dkdv16(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info);
+hipError_t launch_bwd_dq16(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info);
 
 }  // namespace fab

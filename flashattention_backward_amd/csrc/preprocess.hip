@@ -1,5 +1,7 @@
 // Step 1 of the backward (boostr flash_bwd.rs, "Step 1: Preprocessing"):
-//   delta[row] = sum_d dO[row, d] * o[row, d]   (float32), one row per (b, h, query).
+//   D[row] = sum_d dO[row, d] * o[row, d]   (float32), one row per (b, h, query),
+// stored next to the row's LSE rescaled to base 2 (the unit of the kernels' exp2), as the
+// per-row statistics {LSE * log2(e), D} the main kernels stage with each query tile.
 //
 // HBM-bound: each row is read once from each of dO and o.  Lanes load 16 contiguous bytes
 // each, so a wavefront reads whole rows with fully coalesced 16-byte loads; the lanes that
@@ -18,14 +20,18 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const PreParams p) {
   const int tid = threadIdx.x;
   const int sub = tid % L;
   const long long row_base = (long long)blockIdx.x * (ROWS_PER_PASS * PASSES);
+  const long long rows = (long long)p.BH * p.Sq_pad;
   const T* dO = (const T*)p.dO;
   const T* o = (const T*)p.o;
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass) {
-    const long long row = row_base + pass * ROWS_PER_PASS + tid / L;
+    const long long row = row_base + pass * ROWS_PER_PASS + tid / L;  // padded row index
+    const int bh = (int)(row / p.Sq_pad), m = (int)(row % p.Sq_pad);
+    const bool valid = row < rows && m < p.Sq;
+    const long long src_row = (long long)bh * p.Sq + m;
     float acc = 0.f;
-    if (row < p.rows) {
-      const size_t off = (size_t)row * HD + sub * E;
+    if (valid) {
+      const size_t off = (size_t)src_row * HD + sub * E;
       if constexpr (sizeof(T) == 2) {
         typedef T v8 __attribute__((ext_vector_type(8)));
         const v8 a = *reinterpret_cast<const v8*>(dO + off);
@@ -41,14 +47,18 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const PreParams p) {
     }
 #pragma unroll
     for (int w = L / 2; w > 0; w >>= 1) acc += __shfl_xor(acc, w, L);
-    if (sub == 0 && row < p.rows) p.delta[row] = acc;
+    if (sub == 0 && row < rows) {
+      const float l2 = valid ? p.lse[src_row] * kLog2e : __builtin_inff();
+      *reinterpret_cast<float2*>(p.stats + 2 * row) = make_float2(l2, valid ? acc : 0.f);
+    }
   }
 }
 
 template <class T, int HD>
 static hipError_t go(const PreParams& p, hipStream_t s, LaunchInfo* info) {
   constexpr int rows_per_block = (256 / (HD / (16 / sizeof(T)))) * 4;
-  const long long grid = (p.rows + rows_per_block - 1) / rows_per_block;
+  const long long rows = (long long)p.BH * p.Sq_pad;
+  const long long grid = (rows + rows_per_block - 1) / rows_per_block;
   if (info) *info = LaunchInfo{"preprocess", (int)grid, 256, 0};
   hipLaunchKernelGGL((preprocess_kernel<T, HD>), dim3((unsigned)grid), dim3(256), 0, s, p);
   return hipGetLastError();

@@ -62,9 +62,12 @@ const char* fab_version(void);
 const char* fab_last_error(void);
 
 /*
- * Bytes of device workspace fab_bwd needs for these sizes (0 if the sizes are invalid).
- * The workspace holds D = rowsum(dO * O) as float32 [B, H, Sq]; its contents are
- * undefined on entry and on exit.
+ * Bytes of device workspace the backward needs for these sizes (0 if the sizes are invalid).
+ * Layout, as written by the preprocessing step: float32 pairs
+ *   ws[((b * H + h) * Sq_pad + i) * 2 + 0] = lse[b, h, i] * log2(e)
+ *   ws[((b * H + h) * Sq_pad + i) * 2 + 1] = D[b, h, i] = sum_d dO[b,h,i,d] * o[b,h,i,d]
+ * with Sq_pad = Sq rounded up to a multiple of 64; rows i >= Sq hold {+inf, 0}.  fab_bwd
+ * overwrites the workspace on every call; its contents on entry do not matter.
  */
 size_t fab_bwd_workspace_bytes(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype);
 
@@ -81,11 +84,14 @@ fab_status fab_fwd(const void* q, const void* k, const void* v, void* o, float* 
 
 /*
  * Step 1 of the backward on its own (flash_bwd.rs, "Step 1: Preprocessing"):
- *   delta[b, h, i] = sum_d dO[b, h, i, d] * o[b, h, i, d], accumulated in float32.
- * dO, o: [B, H, Sq, D] dtype; delta: [B, H, Sq] float32.  Device pointers, 16-byte
- * aligned.  fab_bwd runs this step itself; it is exported for inspection and timing.
+ *   D[b, h, i] = sum_d dO[b, h, i, d] * o[b, h, i, d], accumulated in float32,
+ * written with the rescaled lse into `workspace` in the layout described at
+ * fab_bwd_workspace_bytes.  dO, o: [B, H, Sq, D] dtype; lse: [B, H, Sq] float32.  Device
+ * pointers, 16-byte aligned.  fab_bwd runs this step itself; it is exported so that D can be
+ * inspected and the step timed, and so that fab_bwd_dkdv / fab_bwd_dq can run on their own.
  */
-fab_status fab_bwd_preprocess(const void* dO, const void* o, float* delta,
+fab_status fab_bwd_preprocess(const void* dO, const void* o, const float* lse,
+                              void* workspace, size_t workspace_bytes,
                               int B, int H, int Sq, int D, int dtype, void* stream);
 
 /*
@@ -111,18 +117,18 @@ fab_status fab_bwd(const void* dO, const void* q, const void* k, const void* v,
 
 /*
  * The two kernels of step 2 on their own, for inspection and per-kernel timing; fab_bwd
- * runs them itself after step 1.  `delta` must hold rowsum(dO * o) as produced by
- * fab_bwd_preprocess for the same dO and o.  Arguments as for fab_bwd.
+ * runs them itself after step 1.  `workspace` must hold what fab_bwd_preprocess wrote for
+ * the same dO, o and lse.  Other arguments as for fab_bwd.
  *   fab_bwd_dkdv writes dk, dv (key-tile outer; each workgroup owns a tile of keys and
  *                sums over every query head of its kv-head group).
  *   fab_bwd_dq   writes dq (query-tile outer; recomputes S and dP for its query rows).
  */
 fab_status fab_bwd_dkdv(const void* dO, const void* q, const void* k, const void* v,
-                        const float* lse, const float* delta, void* dk, void* dv,
+                        const void* workspace, size_t workspace_bytes, void* dk, void* dv,
                         int B, int num_heads, int num_kv_heads, int Sq, int Sk, int D,
                         int dtype, int causal, float scale, void* stream);
 fab_status fab_bwd_dq(const void* dO, const void* q, const void* k, const void* v,
-                      const float* lse, const float* delta, void* dq,
+                      const void* workspace, size_t workspace_bytes, void* dq,
                       int B, int num_heads, int num_kv_heads, int Sq, int Sk, int D,
                       int dtype, int causal, float scale, void* stream);
 

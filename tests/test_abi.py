@@ -28,8 +28,10 @@ def test_exports_every_declared_symbol():
 
 def test_workspace_bytes():
     L = fab.lib()
-    assert L.fab_bwd_workspace_bytes(2, 32, 8, 4096, 4096, 128, 2) == 2 * 32 * 4096 * 4
-    assert L.fab_bwd_workspace_bytes(1, 1, 1, 3, 5, 64, 0) == 256  # rounded up to 256 B
+    # {lse * log2(e), D} per row, rows padded to a multiple of 64, bytes rounded up to 256
+    assert L.fab_bwd_workspace_bytes(2, 32, 8, 4096, 4096, 128, 2) == 2 * 32 * 4096 * 8
+    assert L.fab_bwd_workspace_bytes(1, 1, 1, 3, 5, 64, 0) == 512
+    assert L.fab_bwd_workspace_bytes(1, 3, 3, 65, 5, 64, 0) == 3 * 128 * 8
     assert L.fab_bwd_workspace_bytes(1, 3, 2, 3, 5, 64, 0) == 0    # H % H_kv != 0
     assert L.fab_bwd_workspace_bytes(1, 1, 1, 3, 5, 96, 0) == 0    # head dim
     assert L.fab_bwd_workspace_bytes(1, 1, 1, 3, 5, 64, 9) == 0    # dtype
@@ -78,10 +80,16 @@ def test_fwd_and_preprocess_reject_invalid_arguments():
     assert st == 1 and "v: null" in L.fab_last_error().decode()
     st = L.fab_fwd(P, P, P, P, P, 1, 2, 1, 8, 8, 64, 1, 0, float("nan"), None)
     assert st == 1 and "scale" in L.fab_last_error().decode()
-    st = L.fab_bwd_preprocess(P, P, P + 2, 1, 2, 8, 128, 0, None)
-    assert st == 1 and "delta" in L.fab_last_error().decode()
-    st = L.fab_bwd_preprocess(P, P, P, 1, 2, 8, 32, 0, None)
+    st = L.fab_bwd_preprocess(P, P, P + 2, P, 1 << 30, 1, 2, 8, 128, 0, None)
+    assert st == 1 and "lse" in L.fab_last_error().decode()
+    st = L.fab_bwd_preprocess(P, P, P, P, 16, 1, 2, 8, 128, 0, None)
+    assert st == 1 and "workspace" in L.fab_last_error().decode()
+    st = L.fab_bwd_preprocess(P, P, P, P, 1 << 30, 1, 2, 8, 32, 0, None)
     assert st == 2
+    st = L.fab_bwd_dkdv(P, P, P, P, P, 1 << 30, P, 0, 1, 2, 1, 8, 8, 64, 2, 1, 0.1, None)
+    assert st == 1 and "dv: null" in L.fab_last_error().decode()
+    st = L.fab_bwd_dq(P, P, P, P, P, 8, P, 1, 2, 1, 8, 8, 64, 2, 1, 0.1, None)
+    assert st == 1 and "workspace" in L.fab_last_error().decode()
 
 
 def test_error_message_is_thread_local():

@@ -68,7 +68,7 @@ def test_isolated_backward(fab, dt):
     dev = torch.device("cuda:0")
     dq, dk, dv = fab.bwd(do.to(dev), q.to(dev), k.to(dev), v.to(dev), o.to(dev), lse.to(dev),
                          causal=True, scale=w.scale)
-    delta = fab.bwd_preprocess(do.to(dev), o.to(dev))
+    delta, _ = fab.bwd_preprocess(do.to(dev), o.to(dev), lse.to(dev))
     torch.cuda.synchronize()
     assert_close("delta", to_np64(delta), ref[3], "fp32" if dt == "fp32" else "bf16")
     for name, g, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
