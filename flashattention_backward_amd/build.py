@@ -28,10 +28,16 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
                 "-Wno-unused-command-line-argument"]
 
 
+# Per-source extra flags.  bwd16.hip keeps its long-lived accumulators in AGPRs through
+# inline-asm MFMAs; every other MFMA there is selected in VGPR form so that the short-lived
+# score tiles never compete with the accumulators for AGPRs.
+EXTRA_FLAGS = {"bwd16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *DEVICE_FLAGS, "-I", os.path.join(ROOT, "include"), "-c",
-           os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *DEVICE_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", os.path.join(ROOT, "include"),
+           "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -10,6 +10,8 @@
 //
 // Per-row statistics: stats[(b*H + h) * Sq_pad + i] = {LSE * log2(e), D} with
 // Sq_pad = Sq rounded up to 64 (written by the preprocess kernel).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -177,29 +179,42 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
       // P and dS go straight into the 16-bit operand fragments of the next contractions:
       // fragment (nb, ks) holds accumulator registers 8 ks .. 8 ks + 7 of block nb.
       F pa[2][2], da[2][2];
+      // Key n of block nb may be seen by row m iff n < Sk and (not causal or n <= m).  The
+      // element of row m_base + off (m_base: the row of register 0) is cut iff off < lim[nb]
+      // with lim = +big when n >= Sk, n - m_base when causal, -big otherwise.
+      const int m_base = m0 + 32 * qh + 4 * hl;
+      int lim[2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ml = 32 * qh + 8 * j + 4 * hl;  // first of 4 consecutive rows
-        const f32x4 s01 = *reinterpret_cast<const f32x4*>(st + 2 * ml);
-        const f32x4 s23 = *reinterpret_cast<const f32x4*>(st + 2 * ml + 4);
-        const float l2[4] = {s01[0], s01[2], s23[0], s23[2]};
-        const float dl[4] = {s01[1], s01[3], s23[1], s23[3]};
+      for (int nb = 0; nb < 2; ++nb) {
+        const int n = nw0 + 32 * nb + c32;
+        lim[nb] = n >= Sk ? (1 << 30) : (causal ? n - m_base : -(1 << 30));
+      }
+      auto softmax = [&](auto masked) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * j + e;
+        for (int j = 0; j < 4; ++j) {
+          const int ml = 32 * qh + 8 * j + 4 * hl;  // first of 4 consecutive rows
+          const f32x4 s01 = *reinterpret_cast<const f32x4*>(st + 2 * ml);
+          const f32x4 s23 = *reinterpret_cast<const f32x4*>(st + 2 * ml + 4);
+          const float l2[4] = {s01[0], s01[2], s23[0], s23[2]};
+          const float dl[4] = {s01[1], s01[3], s23[1], s23[3]};
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            float pv = fast_exp2(S[nb][r] * p.scale_log2 - l2[e]);
-            if (need_mask) {
-              const int n = nw0 + 32 * nb + c32;
-              const bool cut = (n >= Sk) | (causal & (n > m0 + ml + e));
-              pv = cut ? 0.f : pv;
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * j + e;
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+              float pv = fast_exp2(S[nb][r] * p.scale_log2 - l2[e]);
+              if constexpr (decltype(masked)::value) {
+                const int off = 8 * j + e;  // row offset of this register from m_base
+                pv = off < lim[nb] ? 0.f : pv;
+              }
+              pa[nb][r >> 3][r & 7] = (T)pv;
+              da[nb][r >> 3][r & 7] = (T)(pv * (dP[nb][r] - dl[e]));
             }
-            pa[nb][r >> 3][r & 7] = (T)pv;
-            da[nb][r >> 3][r & 7] = (T)(pv * (dP[nb][r] - dl[e]));
           }
         }
-      }
+      };
+      if (need_mask) softmax(std::true_type{});
+      else softmax(std::false_type{});
 
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -210,8 +225,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
           const F bq = lds_frag_tr<T>(cur, o_lo, o_hi);
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb) {
-            mma(dv[nb][db], pa[nb][ks], bo);
-            mma(dk[nb][db], da[nb][ks], bq);
+            mma_a(dv[nb][db], pa[nb][ks], bo);
+            mma_a(dk[nb][db], da[nb][ks], bq);
           }
         }
       }
@@ -219,6 +234,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
     wait_vm_all();
     __syncthreads();
   }
+
+  mma_drain(dk[0]);
+  mma_drain(dk[1]);
+  mma_drain(dv[0]);
+  mma_drain(dv[1]);
 
   // ---- epilogue: the qh = 1 waves hand their partial sums to the qh = 0 waves via LDS,
   // which add, scale and store.  The accumulators of a wave pair have identical layouts, so
@@ -396,27 +416,38 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
       }
       const bool need_mask = (n0 + BN > Sk) || (causal && n0 + BN - 1 > mw0);
       F da[2][2];
+      // Register r of this lane holds key n0 + n_base + off(r), off = 8 (r / 4) + r % 4; it
+      // may be seen iff off < lim[mb] = min(Sk, causal ? m + 1 : Sk) - n0 - n_base.
+      const int n_base = 4 * hl;
+      int lim[2];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const int m = mw0 + 32 * mb + c32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pv = fast_exp2(St[mb][r] * p.scale_log2 - lse2[mb]);
-          if (need_mask) {
-            const int n = n0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            const bool cut = (n >= Sk) | (causal & (n > m));
-            pv = cut ? 0.f : pv;
-          }
-          da[mb][r >> 3][r & 7] = (T)(pv * (dPt[mb][r] - dl[mb]));
-        }
+        lim[mb] = (causal ? min(Sk, m + 1) : Sk) - n0 - n_base;
       }
+      auto softmax = [&](auto masked) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float pv = fast_exp2(St[mb][r] * p.scale_log2 - lse2[mb]);
+            if constexpr (decltype(masked)::value) {
+              const int off = 8 * (r >> 2) + (r & 3);
+              pv = off < lim[mb] ? pv : 0.f;
+            }
+            da[mb][r >> 3][r & 7] = (T)(pv * (dPt[mb][r] - dl[mb]));
+          }
+        }
+      };
+      if (need_mask) softmax(std::true_type{});
+      else softmax(std::false_type{});
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const F bk = lds_frag_tr<T>(cur, t_off[db][0] + ks * 16 * RB, t_off[db][1] + ks * 16 * RB);
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb) mma(dq[mb][db], da[mb][ks], bk);
+          for (int mb = 0; mb < 2; ++mb) mma_a(dq[mb][db], da[mb][ks], bk);
         }
       }
     }
@@ -424,6 +455,8 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
     __syncthreads();
   }
 
+  mma_drain(dq[0]);
+  mma_drain(dq[1]);
   T* dQg = (T*)p.dq + q_off * HD;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)

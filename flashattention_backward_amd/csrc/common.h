@@ -46,6 +46,29 @@ __device__ __forceinline__ void mma(f32x16& acc, const f32x8& a, const f32x8& b)
   for (int t = 0; t < 8; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t], b[t], acc, 0, 0, 0);
 }
 
+// acc += A * B with the accumulator pinned to AGPRs (the "a" constraint).  Used for the
+// long-lived accumulators (dK, dV, dQ) so that the register allocator never moves them
+// between the AGPR and VGPR files; the short-lived score tiles use mma() in VGPRs.
+// Hazards handled here, because the compiler does not look inside the asm: `s_nop 1` gives
+// the two wait states needed between a VALU write of an A/B operand and the MFMA reading it;
+// consecutive MFMAs accumulating into the same registers need none; reads of the
+// accumulators after the last MFMA must go through mma_drain() first.
+__device__ __forceinline__ void mma_a(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mma_a(f32x16& acc, const f16x8& a, const f16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Wait states between the last accumulating MFMA and any other access to its registers
+// (more than the 8 passes plus the read latency of a 32x32x16 MFMA).  Every accumulator is an
+// operand, so no accumulating MFMA can be scheduled after the wait and no read before it.
+__device__ __forceinline__ void mma_drain(f32x16 (&a)[4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]));
+}
+__device__ __forceinline__ void mma_drain(f32x16 (&a)[2]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(a[0]), "+a"(a[1]));
+}
+
 // 8 consecutive elements <-> fragment.  16-bit types move as one 16-byte access, fp32 as
 // two, so only 16-byte alignment is ever required.
 template <class T>
