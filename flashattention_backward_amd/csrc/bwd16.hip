@@ -22,24 +22,27 @@ namespace fab {
 // A workgroup owns BN = 128 keys of one (batch, kv head) and walks every query head of the
 // group and every 64-row query tile the causal mask lets reach its keys.  Its 4 waves form a
 // 2 x 2 grid: wave (kb, qh) owns keys [64 kb, 64 kb + 64) and the query rows [32 qh, 32 qh + 32)
-// of each tile, so every Q / dO element read from LDS feeds 64 keys.  K fragments stay in
-// registers, V sits in LDS for the workgroup's life; dK and dV accumulate in registers and
-// the two query halves are summed through LDS at the end.
+// of each tile, so every Q / dO element read from LDS feeds 64 keys.  K and V sit in LDS for
+// the workgroup's life (the register file is taken by the dK, dV accumulators and the score
+// tiles); dK and dV accumulate in AGPRs and the two query halves are summed through LDS at
+// the end.
 // =======================================================================================
 template <int HD>
 struct Dkdv16 {
+  typedef TileLayout<HD> L;
   static constexpr int BN = 128, BM = 64;
-  static constexpr int RB = 2 * HD;            // bytes per tile row
-  static constexpr int GPR = RB / 16;          // 16-byte granules per row
-  static constexpr int TILE = BM * RB;         // one Q or dO tile
+  static constexpr int RB = L::RB;             // bytes per tile row
+  static constexpr int GPR = L::GPR;           // 16-byte granules per row
+  static constexpr int TILE = (BM * RB + 1023) / 1024 * 1024;  // one Q or dO tile (whole KB)
   static constexpr int STATS = BM * 8;         // {lse2, D} per row
   static constexpr int BUF = 2 * TILE + STATS; // one stage: Q, dO, stats
-  static constexpr int VT = BN * RB;           // V tile of the workgroup
-  static constexpr int LDS = 2 * BUF + VT;
+  static constexpr int VT = (BN * RB + 1023) / 1024 * 1024;  // V tile of the workgroup
+  static constexpr int STAGES = 3;             // tiles in flight: current + 2 prefetched
+  static constexpr int LDS = STAGES * BUF + VT;
   static constexpr int RED = 2 * 64 * HD * 4;  // epilogue: two waves' partial dK or dV
+  // Loads one prefetch issues, at least, on every wave (for the in-order vmcnt wait).
+  static constexpr int ISSUE_MIN = 2 * tile_loads_min<HD, BM>(4);
   static_assert(RED <= LDS, "reduction must fit in the staging buffers");
-  static constexpr int QI = TILE / 1024;       // direct-load instructions per Q tile
-  static_assert(QI % 4 == 0, "tile loads split evenly over 4 waves");
 };
 
 template <class T, int HD>
@@ -50,7 +53,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   constexpr int BM = C::BM, BN = C::BN, RB = C::RB;
 
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
-  char* const vtile = smem + 2 * C::BUF;
+  char* const vtile = smem + C::STAGES * C::BUF;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
@@ -67,16 +70,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   const T* Kg = (const T*)p.k + kv_off;
   const T* Vg = (const T*)p.v + kv_off;
 
-  // ---- V tile -> LDS (once), K fragments -> registers (once)
-  {
-    constexpr int VI = C::VT / 1024;  // instructions for the V tile
-    for (int q = w; q < VI; q += 4) {
-      const int gi = 64 * q + lane;
-      const int r = gi / C::GPR, pc = gi % C::GPR;
-      const int n = min(n0 + r, Sk - 1);
-      g2lds16(Vg + (size_t)n * HD + 8 * (pc ^ swz<HD>(r)), vtile + 1024 * q);
-    }
-  }
+  // ---- V tile -> LDS once for the workgroup's life; K fragments -> registers
+  load_tile<T, HD, BN>(vtile, Vg, n0, Sk - 1, w, 4, lane);
   const int nw0 = n0 + 64 * kb;
   F kf[2][NC];
 #pragma unroll
@@ -99,7 +94,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   // A operand (Q or dO rows): row 32 qh + c32, chunk 2 cc + hl
   int a_off[NC];
 #pragma unroll
-  for (int cc = 0; cc < NC; ++cc) a_off[cc] = swz_off<HD>(32 * qh + c32, 2 * cc + hl);
+  for (int cc = 0; cc < NC; ++cc) a_off[cc] = C::L::off(32 * qh + c32, 2 * cc + hl);
   // B operand of P^T dO / dS^T Q, transposed read: 16-lane group (hl, dh), lane i in group
   const int gi16 = lane & 15, dh = (lane >> 4) & 1;
   int t_off[NDB][2];
@@ -109,10 +104,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
     for (int sec = 0; sec < 2; ++sec) {
       const int r = 32 * qh + 4 * hl + 8 * sec + (gi16 >> 2);
       const int col = 32 * db + 16 * dh + 4 * (gi16 & 3);
-      t_off[db][sec] = swz_off<HD>(r, col >> 3) + 2 * (col & 7);
+      t_off[db][sec] = C::L::off(r, col >> 3) + 2 * (col & 7);
     }
-  // B operand of dP = dO V^T: V rows 64 kb + 32 nb + c32 have the same swizzle as the A
-  // operand rows 32 qh + c32 (both are c32 mod 16), so they are a_off plus a wave constant.
+  // B operand of dP = dO V^T: V rows 64 kb + 32 nb + c32 have the same layout offsets as the
+  // A operand rows 32 qh + c32 (both are c32 mod 16), so they are a_off plus a wave constant.
   const char* const vrows = vtile + (64 * kb - 32 * qh) * RB;
 
   // ---- iteration space: (query head in group, query tile), flattened
@@ -121,35 +116,46 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   const int per = n_qt - i_first;
   const int total = G * per;
 
-  auto issue = [&](int s, char* buf) {
+  // Prefetch of the Q, dO tiles and row statistics of step s into a stage buffer, split into
+  // TileDma instructions so that it can be spread over a compute step.
+  TileDma<T, HD, BM> qdma;
+  qdma.init(w, lane);
+  struct Target { const T* q; const T* dO; const float* st; int m0; bool full; };
+  auto target = [&](int s) {
     const int hh = s / per, it = i_first + s % per;
     const int hq = g * G + hh, m0 = it * BM;
     const size_t q_off = (size_t)(b * p.H + hq) * Sq;
-    const T* Qg = (const T*)p.q + q_off * HD;
-    const T* dOg = (const T*)p.dO + q_off * HD;
+    return Target{(const T*)p.q + q_off * HD, (const T*)p.dO + q_off * HD,
+                  p.stats + ((size_t)(b * p.H + hq) * Sq_pad + m0) * 2, m0, m0 + BM <= Sq};
+  };
+  auto issue_part = [&](const Target& t, char* buf, int k) {
+    qdma.issue(k, buf, t.q, t.m0, Sq - 1, t.full);
+    qdma.issue(k, buf + C::TILE, t.dO, t.m0, Sq - 1, t.full);
+    if (k == 0 && w == 0 && lane < C::STATS / 16) g2lds16(t.st + 4 * lane, buf + 2 * C::TILE);
+  };
+  auto issue = [&](int s, char* buf) {
+    const Target t = target(s);
 #pragma unroll
-    for (int k = 0; k < C::QI / 4; ++k) {
-      const int q = w + 4 * k;
-      const int gi = 64 * q + lane;
-      const int r = gi / C::GPR, pc = gi % C::GPR;
-      const size_t src = (size_t)min(m0 + r, Sq - 1) * HD + 8 * (pc ^ swz<HD>(r));
-      g2lds16(Qg + src, buf + 1024 * q);
-      g2lds16(dOg + src, buf + C::TILE + 1024 * q);
-    }
-    if (w == 0 && lane < C::STATS / 16) {
-      const float* st = p.stats + ((size_t)(b * p.H + hq) * Sq_pad + m0) * 2;
-      g2lds16(st + 4 * lane, buf + 2 * C::TILE);
-    }
+    for (int k = 0; k < TileDma<T, HD, BM>::KMAX; ++k) issue_part(t, buf, k);
   };
 
+  // Ring of STAGES tile buffers: step s computes on buffer s % 3 while the tiles of steps
+  // s + 1 and s + 2 are in flight.
   if (total > 0) issue(0, smem);
-  wait_vm_all();
+  if (total > 1) issue(1, smem + C::BUF);
+  if (total > 1) wait_vm_le<C::ISSUE_MIN>();
+  else wait_vm_all();
   __syncthreads();
 
-  for (int s = 0; s < total; ++s) {
-    char* cur = smem + (s & 1) * C::BUF;
-    if (s + 1 < total) issue(s + 1, smem + ((s + 1) & 1) * C::BUF);
-
+  // One step.  The stage being read, the resident V tile and the stage being prefetched are
+  // passed as restrict pointers: the compiler then knows that the direct-to-LDS prefetch does
+  // not write what this step reads, and does not make the step's LDS reads wait for it.
+  auto step_body = [&](const char* __restrict__ cur, const char* __restrict__ vrows,
+                       char* __restrict__ nxt, int s) {
+    // The prefetch of step s + 2 is issued one instruction per head-dim slice of the first
+    // contraction, so the wave never stalls on a burst of memory instructions.
+    const bool pf = s + 2 < total;
+    const Target pt = target(pf ? s + 2 : s);
     const int it = i_first + s % per;
     const int m0 = it * BM;
     const int mw0 = m0 + 32 * qh;
@@ -163,22 +169,37 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
         S[nb] = f32x16{};
         dP[nb] = f32x16{};
       }
+      // Operands of slice cc + 1 are read while the MFMAs of slice cc run.
+      F aq = lds_frag<T>(cur, a_off[0]);
+      F ad = lds_frag<T>(cur + C::TILE, a_off[0]);
+      F bv0 = lds_frag<T>(vrows, a_off[0]);
+      F bv1 = lds_frag<T>(vrows + 32 * RB, a_off[0]);
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) {
-        const F aq = lds_frag<T>(cur, a_off[cc]);
-        const F ad = lds_frag<T>(cur + C::TILE, a_off[cc]);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          mma(S[nb], aq, kf[nb][cc]);
-          mma(dP[nb], ad, lds_frag<T>(vrows + 32 * nb * RB, a_off[cc]));
+        F aq_n, ad_n, bv0_n, bv1_n;
+        if (cc + 1 < NC) {
+          aq_n = lds_frag<T>(cur, a_off[cc + 1]);
+          ad_n = lds_frag<T>(cur + C::TILE, a_off[cc + 1]);
+          bv0_n = lds_frag<T>(vrows, a_off[cc + 1]);
+          bv1_n = lds_frag<T>(vrows + 32 * RB, a_off[cc + 1]);
         }
+        if (pf && cc < TileDma<T, HD, BM>::KMAX) issue_part(pt, nxt, cc);
+        mma(S[0], aq, kf[0][cc]);
+        mma(dP[0], ad, bv0);
+        mma(S[1], aq, kf[1][cc]);
+        mma(dP[1], ad, bv1);
+        if (cc + 1 < NC) {
+          aq = aq_n;
+          ad = ad_n;
+          bv0 = bv0_n;
+          bv1 = bv1_n;
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
 
+      __builtin_amdgcn_sched_barrier(0);
       const bool need_mask = (n0 + BN > Sk) || (causal && nw0 + 63 > mw0);
       const float* st = reinterpret_cast<const float*>(cur + 2 * C::TILE);
-      // P and dS go straight into the 16-bit operand fragments of the next contractions:
-      // fragment (nb, ks) holds accumulator registers 8 ks .. 8 ks + 7 of block nb.
-      F pa[2][2], da[2][2];
       // Key n of block nb may be seen by row m iff n < Sk and (not causal or n <= m).  The
       // element of row m_base + off (m_base: the row of register 0) is cut iff off < lim[nb]
       // with lim = +big when n >= Sk, n - m_base when causal, -big otherwise.
@@ -189,50 +210,107 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
         const int n = nw0 + 32 * nb + c32;
         lim[nb] = n >= Sk ? (1 << 30) : (causal ? n - m_base : -(1 << 30));
       }
-      auto softmax = [&](auto masked) {
+
+      // P and dS go straight into the 16-bit operand fragments of the next contractions:
+      // fragment (nb, ks) holds accumulator registers 8 ks .. 8 ks + 7 of block nb.
+      F pa[2][2], da[2][2];
+      // Row statistics for registers 8 ks .. 8 ks + 7 (rows m_base + 8 j + e, j = 2 ks, 2 ks + 1).
+      auto load_stats = [&](int ks, float (&l2)[8], float (&dl)[8]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int ml = 32 * qh + 8 * j + 4 * hl;  // first of 4 consecutive rows
+        for (int jj = 0; jj < 2; ++jj) {
+          const int ml = 32 * qh + 8 * (2 * ks + jj) + 4 * hl;
           const f32x4 s01 = *reinterpret_cast<const f32x4*>(st + 2 * ml);
           const f32x4 s23 = *reinterpret_cast<const f32x4*>(st + 2 * ml + 4);
-          const float l2[4] = {s01[0], s01[2], s23[0], s23[2]};
-          const float dl[4] = {s01[1], s01[3], s23[1], s23[3]};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * j + e;
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-              float pv = fast_exp2(S[nb][r] * p.scale_log2 - l2[e]);
-              if constexpr (decltype(masked)::value) {
-                const int off = 8 * j + e;  // row offset of this register from m_base
-                pv = off < lim[nb] ? 0.f : pv;
-              }
-              pa[nb][r >> 3][r & 7] = (T)pv;
-              da[nb][r >> 3][r & 7] = (T)(pv * (dP[nb][r] - dl[e]));
-            }
-          }
+          l2[4 * jj + 0] = s01[0]; dl[4 * jj + 0] = s01[1];
+          l2[4 * jj + 1] = s01[2]; dl[4 * jj + 1] = s01[3];
+          l2[4 * jj + 2] = s23[0]; dl[4 * jj + 2] = s23[1];
+          l2[4 * jj + 3] = s23[2]; dl[4 * jj + 3] = s23[3];
         }
       };
-      if (need_mask) softmax(std::true_type{});
-      else softmax(std::false_type{});
-
+      // One element: register r = 8 ks + t of block nb.
+      auto elem = [&](int nb, int ks, int t, const float (&l2)[8], const float (&dl)[8], auto masked) {
+        const int r = 8 * ks + t;
+        float pv = fast_exp2(S[nb][r] * p.scale_log2 - l2[t]);
+        if constexpr (decltype(masked)::value) {
+          const int off = 8 * (r >> 2) + (r & 3);  // row offset of register r from m_base
+          pv = off < lim[nb] ? 0.f : pv;
+        }
+        pa[nb][ks][t] = (T)pv;
+        da[nb][ks][t] = (T)(pv * (dP[nb][r] - dl[t]));
+      };
+      // dV += P^T dO and dK += dS^T Q for one 16-row slice ks of the query rows.  While the
+      // 16 MFMAs of slice 0 run, the softmax of slice 1 (16 elements) is interleaved with them.
+      auto step = [&](auto masked) {
+        float l2[8], dl[8];
+        load_stats(0, l2, dl);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) elem(nb, 0, t, l2, dl, masked);
+        load_stats(1, l2, dl);
+        // Slice 0 MFMAs with the slice 1 softmax woven in; the B operands of the next d block
+        // are read one block ahead.  Scheduling fences keep the compiler from hoisting every
+        // LDS read to the top (which would not fit in the register file).
+        F bo = lds_frag_tr<T>(cur + C::TILE, t_off[0][0], t_off[0][1]);
+        F bq = lds_frag_tr<T>(cur, t_off[0][0], t_off[0][1]);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int o_lo = t_off[db][0] + ks * 16 * RB, o_hi = t_off[db][1] + ks * 16 * RB;
-          const F bo = lds_frag_tr<T>(cur + C::TILE, o_lo, o_hi);
-          const F bq = lds_frag_tr<T>(cur, o_lo, o_hi);
+          F bo_n, bq_n;
+          if (db + 1 < NDB) {
+            bo_n = lds_frag_tr<T>(cur + C::TILE, t_off[db + 1][0], t_off[db + 1][1]);
+            bq_n = lds_frag_tr<T>(cur, t_off[db + 1][0], t_off[db + 1][1]);
+          } else {
+            bo_n = lds_frag_tr<T>(cur + C::TILE, t_off[0][0] + 16 * RB, t_off[0][1] + 16 * RB);
+            bq_n = lds_frag_tr<T>(cur, t_off[0][0] + 16 * RB, t_off[0][1] + 16 * RB);
+          }
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb) {
-            mma_a(dv[nb][db], pa[nb][ks], bo);
-            mma_a(dk[nb][db], da[nb][ks], bq);
+            constexpr int per_db = 16 / NDB;  // slice-1 elements per d block
+            mma_a(dv[nb][db], pa[nb][0], bo);
+#pragma unroll
+            for (int k = 0; k < per_db / 2; ++k) {
+              const int e = db * per_db + nb * (per_db / 2) + k;
+              elem(e & 1, 1, e >> 1, l2, dl, masked);
+            }
+            mma_a(dk[nb][db], da[nb][0], bq);
           }
+          bo = bo_n;
+          bq = bq_n;
+          __builtin_amdgcn_sched_barrier(0);
         }
-      }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          F bo_n, bq_n;
+          if (db + 1 < NDB) {
+            bo_n = lds_frag_tr<T>(cur + C::TILE, t_off[db + 1][0] + 16 * RB, t_off[db + 1][1] + 16 * RB);
+            bq_n = lds_frag_tr<T>(cur, t_off[db + 1][0] + 16 * RB, t_off[db + 1][1] + 16 * RB);
+          }
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            mma_a(dv[nb][db], pa[nb][1], bo);
+            mma_a(dk[nb][db], da[nb][1], bq);
+          }
+          if (db + 1 < NDB) {
+            bo = bo_n;
+            bq = bq_n;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      (void)need_mask;
+      step(std::true_type{});
     }
-    wait_vm_all();
-    __syncthreads();
+  };
+
+  int cb = 0;  // buffer of step s
+  for (int s = 0; s < total; ++s) {
+    const int nb2 = cb >= 1 ? cb - 1 : 2;  // (s + 2) % 3
+    step_body(smem + cb * C::BUF, vrows, smem + nb2 * C::BUF, s);
+    // tile s + 1 must have landed; the loads of tile s + 2 may stay in flight
+    if (s + 2 < total) wait_vm_le<C::ISSUE_MIN>();
+    else wait_vm_all();
+    barrier_lds();
+    cb = cb == 2 ? 0 : cb + 1;
   }
 
   mma_drain(dk[0]);
@@ -294,13 +372,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
 // =======================================================================================
 template <int HD>
 struct Dq16 {
+  typedef TileLayout<HD> L;
   static constexpr int BM = 256, BN = 32;
-  static constexpr int RB = 2 * HD;
-  static constexpr int GPR = RB / 16;
-  static constexpr int TILE = BN * RB;    // one K or V tile
+  static constexpr int RB = L::RB;
+  static constexpr int GPR = L::GPR;
+  static constexpr int TILE = (BN * RB + 1023) / 1024 * 1024;  // one K or V tile (whole KB)
   static constexpr int BUF = 2 * TILE;
-  static constexpr int LDS = 2 * BUF;
-  static constexpr int KI = TILE / 1024;  // direct-load instructions per tile
+  static constexpr int STAGES = 3;
+  static constexpr int LDS = STAGES * BUF;
+  static constexpr int ISSUE_MIN = 2 * tile_loads_min<HD, BN>(4);
 };
 
 template <class T, int HD>
@@ -359,7 +439,7 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
 
   int a_off[NC];
 #pragma unroll
-  for (int cc = 0; cc < NC; ++cc) a_off[cc] = swz_off<HD>(c32, 2 * cc + hl);
+  for (int cc = 0; cc < NC; ++cc) a_off[cc] = C::L::off(c32, 2 * cc + hl);
   const int gi16 = lane & 15, dh = (lane >> 4) & 1;
   int t_off[NDB][2];
 #pragma unroll
@@ -368,34 +448,33 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
     for (int sec = 0; sec < 2; ++sec) {
       const int r = 4 * hl + 8 * sec + (gi16 >> 2);
       const int col = 32 * db + 16 * dh + 4 * (gi16 & 3);
-      t_off[db][sec] = swz_off<HD>(r, col >> 3) + 2 * (col & 7);
+      t_off[db][sec] = C::L::off(r, col >> 3) + 2 * (col & 7);
     }
 
   const int n_kt = (Sk + BN - 1) / BN;
   const int j_end = causal ? min(n_kt, (min(m0 + BM, Sq) - 1) / BN + 1) : n_kt;
 
+  TileDma<T, HD, BN> kvdma;
+  kvdma.init(w, lane);
+  auto issue_part = [&](int j, char* buf, int k) {
+    const bool full = (j + 1) * BN <= Sk;
+    kvdma.issue(k, buf, Kg, j * BN, Sk - 1, full);
+    kvdma.issue(k, buf + C::TILE, Vg, j * BN, Sk - 1, full);
+  };
   auto issue = [&](int j, char* buf) {
-    const int n0 = j * BN;
 #pragma unroll
-    for (int k = 0; k < (2 * C::KI + 3) / 4; ++k) {
-      const int q = w + 4 * k;  // 0..KI-1: K tile, KI..2KI-1: V tile
-      if (q < 2 * C::KI) {
-        const int tq2 = q < C::KI ? q : q - C::KI;
-        const int gi = 64 * tq2 + lane;
-        const int r = gi / C::GPR, pc = gi % C::GPR;
-        const size_t src = (size_t)min(n0 + r, Sk - 1) * HD + 8 * (pc ^ swz<HD>(r));
-        g2lds16((q < C::KI ? Kg : Vg) + src, buf + 1024 * q);
-      }
-    }
+    for (int k = 0; k < TileDma<T, HD, BN>::KMAX; ++k) issue_part(j, buf, k);
   };
 
-  if (j_end > 0) issue(0, smem);
-  wait_vm_all();
+  issue(0, smem);  // j_end >= 1 always
+  if (j_end > 1) issue(1, smem + C::BUF);
+  if (j_end > 1) wait_vm_le<C::ISSUE_MIN>();
+  else wait_vm_all();
   __syncthreads();
 
-  for (int j = 0; j < j_end; ++j) {
-    char* cur = smem + (j & 1) * C::BUF;
-    if (j + 1 < j_end) issue(j + 1, smem + ((j + 1) & 1) * C::BUF);
+  // One step; restrict pointers as in the dK/dV kernel.
+  auto step_body = [&](const char* __restrict__ cur, char* __restrict__ nxt, int j) {
+    const bool pf = j + 2 < j_end;
     const int n0 = j * BN;
     {
       f32x16 St[2], dPt[2];
@@ -408,51 +487,74 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
       for (int cc = 0; cc < NC; ++cc) {
         const F ak = lds_frag<T>(cur, a_off[cc]);
         const F av = lds_frag<T>(cur + C::TILE, a_off[cc]);
+        if (pf && cc < TileDma<T, HD, BN>::KMAX) issue_part(j + 2, nxt, cc);
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
           mma(St[mb], ak, qf[mb][cc]);
           mma(dPt[mb], av, dof[mb][cc]);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      const bool need_mask = (n0 + BN > Sk) || (causal && n0 + BN - 1 > mw0);
+      __builtin_amdgcn_sched_barrier(0);
       F da[2][2];
-      // Register r of this lane holds key n0 + n_base + off(r), off = 8 (r / 4) + r % 4; it
-      // may be seen iff off < lim[mb] = min(Sk, causal ? m + 1 : Sk) - n0 - n_base.
-      const int n_base = 4 * hl;
+      // Register r of this lane holds key n0 + 4 hl + off(r), off = 8 (r / 4) + r % 4; it may
+      // be seen iff off < lim[mb] = min(Sk, causal ? m + 1 : Sk) - n0 - 4 hl.  Applied on every
+      // step (one compare and select per element) so the loop body has a single path.
       int lim[2];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const int m = mw0 + 32 * mb + c32;
-        lim[mb] = (causal ? min(Sk, m + 1) : Sk) - n0 - n_base;
+        lim[mb] = (causal ? min(Sk, m + 1) : Sk) - n0 - 4 * hl;
       }
-      auto softmax = [&](auto masked) {
+      auto elem = [&](int mb, int r) {
+        float pv = fast_exp2(St[mb][r] * p.scale_log2 - lse2[mb]);
+        const int off = 8 * (r >> 2) + (r & 3);
+        pv = off < lim[mb] ? pv : 0.f;
+        da[mb][r >> 3][r & 7] = (T)(pv * (dPt[mb][r] - dl[mb]));
+      };
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) elem(mb, r);
+      // dQ += dS K for key slice 0 with the softmax of slice 1 woven in, then slice 1.
+      F bk = lds_frag_tr<T>(cur, t_off[0][0], t_off[0][1]);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const F bk_n = db + 1 < NDB ? lds_frag_tr<T>(cur, t_off[db + 1][0], t_off[db + 1][1])
+                                    : lds_frag_tr<T>(cur, t_off[0][0] + 16 * RB, t_off[0][1] + 16 * RB);
+        constexpr int per_db = 16 / NDB;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
+          mma_a(dq[mb][db], da[mb][0], bk);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float pv = fast_exp2(St[mb][r] * p.scale_log2 - lse2[mb]);
-            if constexpr (decltype(masked)::value) {
-              const int off = 8 * (r >> 2) + (r & 3);
-              pv = off < lim[mb] ? pv : 0.f;
-            }
-            da[mb][r >> 3][r & 7] = (T)(pv * (dPt[mb][r] - dl[mb]));
+          for (int k = 0; k < per_db / 2; ++k) {
+            const int e = db * per_db + mb * (per_db / 2) + k;  // 0..15 over slice 1
+            elem(e >> 3, 8 + (e & 7));
           }
         }
-      };
-      if (need_mask) softmax(std::true_type{});
-      else softmax(std::false_type{});
+        bk = bk_n;
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int db = 0; db < NDB; ++db) {
+        F bk_n;
+        if (db + 1 < NDB) bk_n = lds_frag_tr<T>(cur, t_off[db + 1][0] + 16 * RB, t_off[db + 1][1] + 16 * RB);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const F bk = lds_frag_tr<T>(cur, t_off[db][0] + ks * 16 * RB, t_off[db][1] + ks * 16 * RB);
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb) mma_a(dq[mb][db], da[mb][ks], bk);
-        }
+        for (int mb = 0; mb < 2; ++mb) mma_a(dq[mb][db], da[mb][1], bk);
+        if (db + 1 < NDB) bk = bk_n;
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    wait_vm_all();
-    __syncthreads();
+  };
+
+  int cb = 0;
+  for (int j = 0; j < j_end; ++j) {
+    const int nb2 = cb >= 1 ? cb - 1 : 2;
+    step_body(smem + cb * C::BUF, smem + nb2 * C::BUF, j);
+    if (j + 2 < j_end) wait_vm_le<C::ISSUE_MIN>();
+    else wait_vm_all();
+    barrier_lds();
+    cb = cb == 2 ? 0 : cb + 1;
   }
 
   mma_drain(dq[0]);

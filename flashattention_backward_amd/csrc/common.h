@@ -136,20 +136,34 @@ __device__ __forceinline__ int perm16(int m) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------------------
-// Swizzled 16-bit tiles in LDS.  A tile row holds HD elements (2*HD bytes, no padding); the
-// 16-byte chunk c of row r is stored at chunk position c ^ swz<HD>(r).  The XOR pattern is
-// chosen so that both access shapes the kernels use are free of bank conflicts on gfx950
-// (measured): a b128 read of one chunk from 32 consecutive rows, and a ds_read_b64_tr_b16
-// of a 4-row x 16-column block by each 16-lane group.
+// 16-bit tiles in LDS.  Both access shapes the kernels use must be free of bank conflicts on
+// gfx950: a b128 read of one 16-byte chunk from 32 consecutive rows (operands that contract
+// over the head dim) and a ds_read_b64_tr_b16 of a 4-row x 16-column block per 16-lane group
+// (operands that contract over rows).  Measured layouts that satisfy both:
+//   HD = 128: rows padded to 304 bytes (16 data chunks + 3 pad chunks), chunk c at 16 c;
+//   HD = 64:  unpadded 128-byte rows, chunk c stored at position c ^ swz64(r).
+// Padding keeps every per-lane offset affine in the chunk index, so unrolled loops address
+// the tile with one base register and immediate offsets.
+__device__ __forceinline__ int swz64(int r) { return 4 * ((r >> 1) & 1) + ((r >> 2) & 3); }
+
 template <int HD>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (HD == 128) return 4 * (r & 3) + ((r >> 2) & 3);
-  else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
-}
-template <int HD>
-__device__ __forceinline__ int swz_off(int r, int c) {
-  return r * (2 * HD) + 16 * (c ^ swz<HD>(r));
-}
+struct TileLayout {
+  static constexpr bool kPadded = HD == 128;
+  static constexpr int RB = kPadded ? 304 : 2 * HD;  // bytes per row
+  static constexpr int GPR = RB / 16;                // 16-byte granules per row, padding included
+  static constexpr int CPR = 2 * HD / 16;            // data chunks per row
+  // Byte offset of 16-byte chunk c of row r.
+  __device__ static __forceinline__ int off(int r, int c) {
+    if constexpr (kPadded) return r * RB + 16 * c;
+    else return r * RB + 16 * (c ^ swz64(r));
+  }
+  // Which data chunk of row r granule position pc holds (padding granules repeat chunks
+  // 0..2 of the row, so that every granule of a tile row can be loaded from valid memory).
+  __device__ static __forceinline__ int chunk_at(int r, int pc) {
+    if constexpr (kPadded) return pc < CPR ? pc : pc - CPR;
+    else return pc ^ swz64(r);
+  }
+};
 
 typedef __attribute__((address_space(3))) char lds_char;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -179,7 +193,96 @@ __device__ __forceinline__ void g2lds16(const void* src, char* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_char*)lds_wave_base, 16, 0, 0);
 }
 
+// Copy rows [row0, row0 + ROWS) of a row-major [*, HD] tensor into an LDS tile in
+// TileLayout<HD>, with direct global->LDS loads spread over `nw` waves (this one is wave w).
+// Rows past `last_row` are loaded from `last_row` (finite data; callers mask them).
+template <class T, int HD, int ROWS>
+__device__ __forceinline__ void load_tile(char* tile, const T* src, int row0, int last_row,
+                                          int w, int nw, int lane) {
+  typedef TileLayout<HD> L;
+  constexpr int NG = ROWS * L::GPR;      // granules in the tile
+  constexpr int NI = (NG + 63) / 64;     // wave instructions (1 KB each)
+#pragma unroll
+  for (int k = 0; k < (NI + 3) / 4; ++k) {
+    const int q = w + nw * k;
+    if (q < NI) {
+      const int gi = 64 * q + lane;
+      if (NG % 64 == 0 || gi < NG) {
+        const int r = gi / L::GPR, pc = gi % L::GPR;
+        const int row = min(row0 + r, last_row);
+        g2lds16(src + (size_t)row * HD + 8 * L::chunk_at(r, pc), tile + 1024 * q);
+      }
+    }
+  }
+}
+
+// The same copy split into single instructions, so that a prefetch can be spread over a
+// compute step instead of stalling the wave's issue at one point.  Per-lane granule offsets
+// (element offset of the granule within the tile's source rows) are computed once.
+template <class T, int HD, int ROWS>
+struct TileDma {
+  typedef TileLayout<HD> L;
+  static constexpr int NG = ROWS * L::GPR;
+  static constexpr int NI = (NG + 63) / 64;   // wave instructions for the whole tile
+  static constexpr int KMAX = (NI + 3) / 4;   // most instructions any of 4 waves issues
+  int w;
+  unsigned src_off[KMAX];  // r * HD + 8 * chunk for this lane's granule of instruction k
+  int row_of[KMAX];        // tile row of that granule
+  bool valid[KMAX];        // this lane's granule exists (last instruction may be partial)
+  __device__ __forceinline__ void init(int wave, int lane) {
+    w = wave;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      const int gi = 64 * (w + 4 * k) + lane;
+      const int r = gi / L::GPR, pc = gi % L::GPR;
+      row_of[k] = r;
+      valid[k] = gi < NG;
+      src_off[k] = (unsigned)(r * HD + 8 * L::chunk_at(r, pc));
+    }
+  }
+  __device__ __forceinline__ bool has(int k) const { return w + 4 * k < NI; }
+  // Instruction k of this wave: rows row0 .. row0 + ROWS - 1 of src into `tile`; rows past
+  // last_row are read from last_row.  `full` (uniform): no row needs clamping.
+  __device__ __forceinline__ void issue(int k, char* tile, const T* src, int row0, int last_row,
+                                        bool full) const {
+    if (!has(k)) return;
+    char* dst = tile + 1024 * (w + 4 * k);
+    if (NG % 64 != 0 && !valid[k]) return;
+    if (full) {
+      g2lds16(src + (size_t)row0 * HD + src_off[k], dst);
+    } else {
+      const int row = min(row0 + row_of[k], last_row);
+      g2lds16(src + (size_t)row * HD + (src_off[k] - (unsigned)(row_of[k] * HD)), dst);
+    }
+  }
+};
+
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier for the staging loops.  __syncthreads() also waits for every outstanding
+// global memory operation of the wave (vmcnt(0)), which would stall on the tiles being
+// prefetched; here each wave first drains only its LDS reads (so no wave can still be reading
+// a buffer that the next step's prefetch overwrites) and the caller waits explicitly for the
+// tile the next step needs (wait_vm_le).  The empty asm blocks with a memory clobber stop
+// the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding (loads return
+// in order, so everything issued before the last N has landed).  gfx9 s_waitcnt encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at "no wait".
+template <int N>
+__device__ __forceinline__ void wait_vm_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Fewest direct-load instructions any of `nw` waves issues for a tile of ROWS rows.
+template <int HD, int ROWS>
+constexpr int tile_loads_min(int nw) {
+  return ((ROWS * TileLayout<HD>::GPR + 63) / 64) / nw;
+}
 
 // Work-item mapping shared by the launches: workgroup ids are dispatched round-robin over
 // the 8 XCDs, so id w runs on XCD w % 8.  When the independent units (kv-head groups) split
