@@ -6,6 +6,7 @@
 // sizes can express; the Python binding checks tensor shapes, strides and devices.
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -66,6 +67,10 @@ fab_status check_common(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype
                 "num_heads %d is not a multiple of num_kv_heads %d", H, H_kv);
   if ((long long)B * H * Sq * D > kMaxElems || (long long)B * H_kv * Sk * D > kMaxElems)
     return fail(FAB_ERR_INVALID_ARGUMENT, "dims", "a tensor exceeds 2^31-1 elements");
+  // The kernels address the row statistics of one kv-head group with 32-bit byte offsets.
+  if ((long long)(H / H_kv) * fab::stats_rows(Sq) * 8 > 0xFFFFFFFFLL)
+    return fail(FAB_ERR_UNSUPPORTED, "dims",
+                "num_heads / num_kv_heads * Sq too large (%d query heads per kv head, Sq=%d)", H / H_kv, Sq);
   return FAB_OK;
 }
 
@@ -122,7 +127,14 @@ fab::BwdParams bwd_params(const void* dO, const void* q, const void* k, const vo
   p.B = B; p.H = H; p.H_kv = H_kv; p.Sq = Sq; p.Sk = Sk; p.Sq_pad = fab::stats_rows(Sq);
   p.causal = causal ? 1 : 0;
   p.scale = scale;
-  p.scale_log2 = scale * fab::kLog2eHost;
+  // The kernels mask a score by replacing it with mask_s, for which mask_s * scale_log2 is
+  // -inf.  A zero (or subnormal) exponent scale is raised to the smallest normal float of the
+  // same sign so that this product is never 0 * inf; the scores it multiplies are finite, and
+  // s * FLT_MIN is far below the resolution of the exponent's other term.
+  float sl2 = scale * fab::kLog2eHost;
+  if (std::fabs(sl2) < FLT_MIN) sl2 = std::signbit(sl2) ? -FLT_MIN : FLT_MIN;
+  p.scale_log2 = sl2;
+  p.mask_s = sl2 > 0.f ? -INFINITY : INFINITY;
   p.n_units = B * H_kv;
   p.units_per_xcd = units_per_xcd(p.n_units);
   return p;

@@ -1,8 +1,8 @@
 // The two step-2 kernels for 16-bit inputs (bf16, fp16), tiled for gfx950.
 //
 // Both kernels stage their streamed operand tiles with direct global->LDS loads
-// (global_load_lds_dwordx4) into a double buffer, so the next tile arrives while the current
-// one is consumed and each step needs one barrier.  Tiles are row-major and XOR-swizzled
+// (buffer_load_dwordx4 ... lds) into a ring of stage buffers, so the next tiles arrive while
+// the current one is consumed and each step needs one barrier.  Tiles are row-major and XOR-swizzled
 // (swz in common.h); operands that contract over rows are read with the LDS transpose read
 // (lds_frag_tr) instead of keeping a transposed copy.  Rows past the end of a sequence are
 // loaded from the last valid row (finite data) and neutralised by the masks and by the
@@ -32,28 +32,34 @@ struct Dkdv16 {
   typedef TileLayout<HD> L;
   static constexpr int BN = 128, BM = 64;
   static constexpr int RB = L::RB;             // bytes per tile row
-  static constexpr int GPR = L::GPR;           // 16-byte granules per row
   static constexpr int TILE = (BM * RB + 1023) / 1024 * 1024;  // one Q or dO tile (whole KB)
-  static constexpr int STATS = BM * 8;         // {lse2, D} per row
+  static constexpr int STATS = 1024;           // {lse2, D} of 128 rows (one wave-wide load)
   static constexpr int BUF = 2 * TILE + STATS; // one stage: Q, dO, stats
   static constexpr int VT = (BN * RB + 1023) / 1024 * 1024;  // V tile of the workgroup
   static constexpr int STAGES = 3;             // tiles in flight: current + 2 prefetched
-  static constexpr int LDS = STAGES * BUF + VT;
+  static constexpr int SPARE = 1024;           // target of the padding loads (never read)
+  static constexpr int LDS = STAGES * BUF + VT + SPARE;
   static constexpr int RED = 2 * 64 * HD * 4;  // epilogue: two waves' partial dK or dV
-  // Loads one prefetch issues, at least, on every wave (for the in-order vmcnt wait).
-  static constexpr int ISSUE_MIN = 2 * tile_loads_min<HD, BM>(4);
+  typedef TileDma<bf16, HD, BM> Dma;           // (the element type only sets the row size)
+  static constexpr int KMAX = Dma::KMAX;
+  // Loads each wave issues per stage (Q and dO; wave 0 adds the statistics).
+  static constexpr int ISSUE = 2 * KMAX;
   static_assert(RED <= LDS, "reduction must fit in the staging buffers");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
 template <class T, int HD>
 __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   typedef Dkdv16<HD> C;
   typedef typename Frag<T>::type F;
+  typedef TileDma<T, HD, Dkdv16<HD>::BM> Dma;
   constexpr int NC = HD / 16, NDB = HD / 32;
   constexpr int BM = C::BM, BN = C::BN, RB = C::RB;
+  constexpr unsigned ROWB = HD * sizeof(T);
 
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
   char* const vtile = smem + C::STAGES * C::BUF;
+  char* const spare = vtile + C::VT;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
@@ -110,208 +116,217 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   // A operand rows 32 qh + c32 (both are c32 mod 16), so they are a_off plus a wave constant.
   const char* const vrows = vtile + (64 * kb - 32 * qh) * RB;
 
-  // ---- iteration space: (query head in group, query tile), flattened
+  // ---- iteration space: every query head of the group and every query tile whose rows
+  // the causal mask lets reach these keys; step s is head s / per, tile i_first + s % per.
   const int n_qt = (Sq + BM - 1) / BM;
   const int i_first = causal ? min(n0 / BM, n_qt) : 0;
   const int per = n_qt - i_first;
   const int total = G * per;
 
-  // Prefetch of the Q, dO tiles and row statistics of step s into a stage buffer, split into
-  // TileDma instructions so that it can be spread over a compute step.
-  TileDma<T, HD, BM> qdma;
+  // Buffer resources over the rows of the group's query heads (Q, dO) and their row
+  // statistics.  A tile is selected by a uniform byte offset; rows past a head's end read the
+  // next head's rows or, past the group, zeros: finite values that the padding rows'
+  // statistics (lse = +inf) turn into P = 0.  The prefetch issued after the last step reads
+  // past the group (zeros) into a stage nothing reads any more.
+  const size_t row0 = (size_t)(b * p.H + g * G) * Sq;
+  const rsrc_t rq = make_rsrc((const T*)p.q + row0 * HD, (unsigned)((size_t)G * Sq * ROWB));
+  const rsrc_t rdo = make_rsrc((const T*)p.dO + row0 * HD, (unsigned)((size_t)G * Sq * ROWB));
+  const rsrc_t rst = make_rsrc(p.stats + (size_t)(b * p.H + g * G) * Sq_pad * 2,
+                               (unsigned)((size_t)G * Sq_pad * 8));
+
+  Dma qdma;
   qdma.init(w, lane);
-  struct Target { const T* q; const T* dO; const float* st; int m0; bool full; };
-  auto target = [&](int s) {
-    const int hh = s / per, it = i_first + s % per;
-    const int hq = g * G + hh, m0 = it * BM;
-    const size_t q_off = (size_t)(b * p.H + hq) * Sq;
-    return Target{(const T*)p.q + q_off * HD, (const T*)p.dO + q_off * HD,
-                  p.stats + ((size_t)(b * p.H + hq) * Sq_pad + m0) * 2, m0, m0 + BM <= Sq};
+  // Head and tile of the next stage to prefetch, advanced once per issued stage.
+  int ph = 0, pit = i_first;
+  auto issue_part = [&](char* buf, int k, unsigned q_soff, unsigned st_soff) {
+    qdma.issue(k, buf, rq, q_soff, spare);
+    qdma.issue(k, buf + C::TILE, rdo, q_soff, spare);
+    if (k == 0 && w == 0) b2lds16(rst, 16u * lane, st_soff, buf + 2 * C::TILE);
   };
-  auto issue_part = [&](const Target& t, char* buf, int k) {
-    qdma.issue(k, buf, t.q, t.m0, Sq - 1, t.full);
-    qdma.issue(k, buf + C::TILE, t.dO, t.m0, Sq - 1, t.full);
-    if (k == 0 && w == 0 && lane < C::STATS / 16) g2lds16(t.st + 4 * lane, buf + 2 * C::TILE);
+  auto next_offsets = [&](unsigned& q_soff, unsigned& st_soff) {
+    q_soff = (unsigned)(ph * Sq + pit * BM) * ROWB;
+    st_soff = (unsigned)(ph * Sq_pad + pit * BM) * 8u;
+    if (++pit == n_qt) {
+      pit = i_first;
+      ++ph;
+    }
   };
-  auto issue = [&](int s, char* buf) {
-    const Target t = target(s);
+  auto issue = [&](char* buf) {
+    unsigned qs, ss;
+    next_offsets(qs, ss);
 #pragma unroll
-    for (int k = 0; k < TileDma<T, HD, BM>::KMAX; ++k) issue_part(t, buf, k);
+    for (int k = 0; k < C::KMAX; ++k) issue_part(buf, k, qs, ss);
   };
 
   // Ring of STAGES tile buffers: step s computes on buffer s % 3 while the tiles of steps
   // s + 1 and s + 2 are in flight.
-  if (total > 0) issue(0, smem);
-  if (total > 1) issue(1, smem + C::BUF);
-  if (total > 1) wait_vm_le<C::ISSUE_MIN>();
-  else wait_vm_all();
-  __syncthreads();
+  issue(smem);
+  issue(smem + C::BUF);
+  wait_vm_le<C::ISSUE>();  // V, K and stage 0 have landed
+  barrier_lds();
+
+  const float mask_s = p.mask_s;
 
   // One step.  The stage being read, the resident V tile and the stage being prefetched are
   // passed as restrict pointers: the compiler then knows that the direct-to-LDS prefetch does
   // not write what this step reads, and does not make the step's LDS reads wait for it.
   auto step_body = [&](const char* __restrict__ cur, const char* __restrict__ vrows,
-                       char* __restrict__ nxt, int s) {
+                       char* __restrict__ nxt, int m0) {
     // The prefetch of step s + 2 is issued one instruction per head-dim slice of the first
     // contraction, so the wave never stalls on a burst of memory instructions.
-    const bool pf = s + 2 < total;
-    const Target pt = target(pf ? s + 2 : s);
-    const int it = i_first + s % per;
-    const int m0 = it * BM;
+    unsigned pq_soff, pst_soff;
+    next_offsets(pq_soff, pst_soff);
     const int mw0 = m0 + 32 * qh;
-    // Every wave computes every step (a wave whose keys all lie after its rows gets P = 0
-    // from the mask): the workgroup waits for its slowest wave at the barrier anyway, and
-    // branch-free accumulation keeps the accumulators in place.
-    {
-      f32x16 S[2], dP[2];
+    f32x16 S[2], dP[2];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        S[nb] = f32x16{};
-        dP[nb] = f32x16{};
-      }
-      // Operands of slice cc + 1 are read while the MFMAs of slice cc run.
-      F aq = lds_frag<T>(cur, a_off[0]);
-      F ad = lds_frag<T>(cur + C::TILE, a_off[0]);
-      F bv0 = lds_frag<T>(vrows, a_off[0]);
-      F bv1 = lds_frag<T>(vrows + 32 * RB, a_off[0]);
+    for (int nb = 0; nb < 2; ++nb) {
+      S[nb] = f32x16{};
+      dP[nb] = f32x16{};
+    }
+    // Operands of slice cc + 1 are read while the MFMAs of slice cc run.
+    F aq = lds_frag<T>(cur, a_off[0]);
+    F ad = lds_frag<T>(cur + C::TILE, a_off[0]);
+    F bv0 = lds_frag<T>(vrows, a_off[0]);
+    F bv1 = lds_frag<T>(vrows + 32 * RB, a_off[0]);
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) {
-        F aq_n, ad_n, bv0_n, bv1_n;
-        if (cc + 1 < NC) {
-          aq_n = lds_frag<T>(cur, a_off[cc + 1]);
-          ad_n = lds_frag<T>(cur + C::TILE, a_off[cc + 1]);
-          bv0_n = lds_frag<T>(vrows, a_off[cc + 1]);
-          bv1_n = lds_frag<T>(vrows + 32 * RB, a_off[cc + 1]);
-        }
-        if (pf && cc < TileDma<T, HD, BM>::KMAX) issue_part(pt, nxt, cc);
-        mma(S[0], aq, kf[0][cc]);
-        mma(dP[0], ad, bv0);
-        mma(S[1], aq, kf[1][cc]);
-        mma(dP[1], ad, bv1);
-        if (cc + 1 < NC) {
-          aq = aq_n;
-          ad = ad_n;
-          bv0 = bv0_n;
-          bv1 = bv1_n;
-        }
-        __builtin_amdgcn_sched_barrier(0);
+    for (int cc = 0; cc < NC; ++cc) {
+      F aq_n, ad_n, bv0_n, bv1_n;
+      if (cc + 1 < NC) {
+        aq_n = lds_frag<T>(cur, a_off[cc + 1]);
+        ad_n = lds_frag<T>(cur + C::TILE, a_off[cc + 1]);
+        bv0_n = lds_frag<T>(vrows, a_off[cc + 1]);
+        bv1_n = lds_frag<T>(vrows + 32 * RB, a_off[cc + 1]);
       }
-
+      if (cc < C::KMAX) issue_part(nxt, cc, pq_soff, pst_soff);
+      mma(S[0], aq, kf[0][cc]);
+      mma(dP[0], ad, bv0);
+      mma(S[1], aq, kf[1][cc]);
+      mma(dP[1], ad, bv1);
+      if (cc + 1 < NC) {
+        aq = aq_n;
+        ad = ad_n;
+        bv0 = bv0_n;
+        bv1 = bv1_n;
+      }
       __builtin_amdgcn_sched_barrier(0);
-      const bool need_mask = (n0 + BN > Sk) || (causal && nw0 + 63 > mw0);
-      const float* st = reinterpret_cast<const float*>(cur + 2 * C::TILE);
-      // Key n of block nb may be seen by row m iff n < Sk and (not causal or n <= m).  The
-      // element of row m_base + off (m_base: the row of register 0) is cut iff off < lim[nb]
-      // with lim = +big when n >= Sk, n - m_base when causal, -big otherwise.
-      const int m_base = m0 + 32 * qh + 4 * hl;
-      int lim[2];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Masking, only on steps that need it (the causal diagonal, the last key tile): a cut
+    // score is replaced by mask_s, whose exponent is -inf, so P = 0 and dS = 0 there.  Key n
+    // (this lane's column of block nb) may be seen by row m iff n < Sk and (not causal or
+    // n <= m); register r holds row m_base + off(r), off(r) = 8 (r / 4) + r % 4.
+    if ((n0 + BN > Sk) || (causal && nw0 + 63 > mw0)) {
+      const int m_base = mw0 + 4 * hl;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const int n = nw0 + 32 * nb + c32;
-        lim[nb] = n >= Sk ? (1 << 30) : (causal ? n - m_base : -(1 << 30));
+        const int lim = n >= Sk ? (1 << 30) : (causal ? n - m_base : -(1 << 30));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = 8 * (r >> 2) + (r & 3);
+          S[nb][r] = off < lim ? mask_s : S[nb][r];
+        }
       }
+    }
 
-      // P and dS go straight into the 16-bit operand fragments of the next contractions:
-      // fragment (nb, ks) holds accumulator registers 8 ks .. 8 ks + 7 of block nb.
-      F pa[2][2], da[2][2];
-      // Row statistics for registers 8 ks .. 8 ks + 7 (rows m_base + 8 j + e, j = 2 ks, 2 ks + 1).
-      auto load_stats = [&](int ks, float (&l2)[8], float (&dl)[8]) {
+    const float* st = reinterpret_cast<const float*>(cur + 2 * C::TILE);
+    // P and dS go straight into the 16-bit operand fragments of the next contractions:
+    // fragment (nb, ks) holds accumulator registers 8 ks .. 8 ks + 7 of block nb.
+    F pa[2][2], da[2][2];
+    // Row statistics for registers 8 ks .. 8 ks + 7 (rows m_base + 8 j + e, j = 2 ks, 2 ks + 1).
+    auto load_stats = [&](int ks, float (&l2)[8], float (&dl)[8]) {
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int ml = 32 * qh + 8 * (2 * ks + jj) + 4 * hl;
-          const f32x4 s01 = *reinterpret_cast<const f32x4*>(st + 2 * ml);
-          const f32x4 s23 = *reinterpret_cast<const f32x4*>(st + 2 * ml + 4);
-          l2[4 * jj + 0] = s01[0]; dl[4 * jj + 0] = s01[1];
-          l2[4 * jj + 1] = s01[2]; dl[4 * jj + 1] = s01[3];
-          l2[4 * jj + 2] = s23[0]; dl[4 * jj + 2] = s23[1];
-          l2[4 * jj + 3] = s23[2]; dl[4 * jj + 3] = s23[3];
+      for (int jj = 0; jj < 2; ++jj) {
+        const int ml = 32 * qh + 8 * (2 * ks + jj) + 4 * hl;
+        const f32x4 s01 = *reinterpret_cast<const f32x4*>(st + 2 * ml);
+        const f32x4 s23 = *reinterpret_cast<const f32x4*>(st + 2 * ml + 4);
+        l2[4 * jj + 0] = s01[0]; dl[4 * jj + 0] = s01[1];
+        l2[4 * jj + 1] = s01[2]; dl[4 * jj + 1] = s01[3];
+        l2[4 * jj + 2] = s23[0]; dl[4 * jj + 2] = s23[1];
+        l2[4 * jj + 3] = s23[2]; dl[4 * jj + 3] = s23[3];
+      }
+    };
+    // One element: register r = 8 ks + t of block nb.
+    auto elem = [&](int nb, int ks, int t, const float (&l2)[8], const float (&dl)[8]) {
+      const int r = 8 * ks + t;
+      const float pv = fast_exp2(S[nb][r] * p.scale_log2 - l2[t]);
+      pa[nb][ks][t] = (T)pv;
+      da[nb][ks][t] = (T)(pv * (dP[nb][r] - dl[t]));
+    };
+    // dV += P^T dO and dK += dS^T Q for one 16-row slice ks of the query rows.  While the
+    // 16 MFMAs of slice 0 run, the softmax of slice 1 (16 elements) is interleaved with them.
+    float l2[8], dl[8];
+    load_stats(0, l2, dl);
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) elem(nb, 0, t, l2, dl);
+    load_stats(1, l2, dl);
+    // Slice 0 MFMAs with the slice 1 softmax woven in; the B operands of the next d block
+    // are read one block ahead.  Scheduling fences keep the compiler from hoisting every
+    // LDS read to the top (which would not fit in the register file).
+    F bo = lds_frag_tr<T>(cur + C::TILE, t_off[0][0], t_off[0][1]);
+    F bq = lds_frag_tr<T>(cur, t_off[0][0], t_off[0][1]);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      F bo_n, bq_n;
+      if (db + 1 < NDB) {
+        bo_n = lds_frag_tr<T>(cur + C::TILE, t_off[db + 1][0], t_off[db + 1][1]);
+        bq_n = lds_frag_tr<T>(cur, t_off[db + 1][0], t_off[db + 1][1]);
+      } else {
+        bo_n = lds_frag_tr<T>(cur + C::TILE, t_off[0][0] + 16 * RB, t_off[0][1] + 16 * RB);
+        bq_n = lds_frag_tr<T>(cur, t_off[0][0] + 16 * RB, t_off[0][1] + 16 * RB);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        constexpr int per_db = 16 / NDB;  // slice-1 elements per d block
+        mma_a(dv[nb][db], pa[nb][0], bo);
+#pragma unroll
+        for (int k = 0; k < per_db / 2; ++k) {
+          const int e = db * per_db + nb * (per_db / 2) + k;
+          elem(e & 1, 1, e >> 1, l2, dl);
         }
-      };
-      // One element: register r = 8 ks + t of block nb.
-      auto elem = [&](int nb, int ks, int t, const float (&l2)[8], const float (&dl)[8], auto masked) {
-        const int r = 8 * ks + t;
-        float pv = fast_exp2(S[nb][r] * p.scale_log2 - l2[t]);
-        if constexpr (decltype(masked)::value) {
-          const int off = 8 * (r >> 2) + (r & 3);  // row offset of register r from m_base
-          pv = off < lim[nb] ? 0.f : pv;
-        }
-        pa[nb][ks][t] = (T)pv;
-        da[nb][ks][t] = (T)(pv * (dP[nb][r] - dl[t]));
-      };
-      // dV += P^T dO and dK += dS^T Q for one 16-row slice ks of the query rows.  While the
-      // 16 MFMAs of slice 0 run, the softmax of slice 1 (16 elements) is interleaved with them.
-      auto step = [&](auto masked) {
-        float l2[8], dl[8];
-        load_stats(0, l2, dl);
+        mma_a(dk[nb][db], da[nb][0], bq);
+      }
+      bo = bo_n;
+      bq = bq_n;
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
+    for (int db = 0; db < NDB; ++db) {
+      F bo_n, bq_n;
+      if (db + 1 < NDB) {
+        bo_n = lds_frag_tr<T>(cur + C::TILE, t_off[db + 1][0] + 16 * RB, t_off[db + 1][1] + 16 * RB);
+        bq_n = lds_frag_tr<T>(cur, t_off[db + 1][0] + 16 * RB, t_off[db + 1][1] + 16 * RB);
+      }
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) elem(nb, 0, t, l2, dl, masked);
-        load_stats(1, l2, dl);
-        // Slice 0 MFMAs with the slice 1 softmax woven in; the B operands of the next d block
-        // are read one block ahead.  Scheduling fences keep the compiler from hoisting every
-        // LDS read to the top (which would not fit in the register file).
-        F bo = lds_frag_tr<T>(cur + C::TILE, t_off[0][0], t_off[0][1]);
-        F bq = lds_frag_tr<T>(cur, t_off[0][0], t_off[0][1]);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          F bo_n, bq_n;
-          if (db + 1 < NDB) {
-            bo_n = lds_frag_tr<T>(cur + C::TILE, t_off[db + 1][0], t_off[db + 1][1]);
-            bq_n = lds_frag_tr<T>(cur, t_off[db + 1][0], t_off[db + 1][1]);
-          } else {
-            bo_n = lds_frag_tr<T>(cur + C::TILE, t_off[0][0] + 16 * RB, t_off[0][1] + 16 * RB);
-            bq_n = lds_frag_tr<T>(cur, t_off[0][0] + 16 * RB, t_off[0][1] + 16 * RB);
-          }
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            constexpr int per_db = 16 / NDB;  // slice-1 elements per d block
-            mma_a(dv[nb][db], pa[nb][0], bo);
-#pragma unroll
-            for (int k = 0; k < per_db / 2; ++k) {
-              const int e = db * per_db + nb * (per_db / 2) + k;
-              elem(e & 1, 1, e >> 1, l2, dl, masked);
-            }
-            mma_a(dk[nb][db], da[nb][0], bq);
-          }
-          bo = bo_n;
-          bq = bq_n;
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          F bo_n, bq_n;
-          if (db + 1 < NDB) {
-            bo_n = lds_frag_tr<T>(cur + C::TILE, t_off[db + 1][0] + 16 * RB, t_off[db + 1][1] + 16 * RB);
-            bq_n = lds_frag_tr<T>(cur, t_off[db + 1][0] + 16 * RB, t_off[db + 1][1] + 16 * RB);
-          }
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            mma_a(dv[nb][db], pa[nb][1], bo);
-            mma_a(dk[nb][db], da[nb][1], bq);
-          }
-          if (db + 1 < NDB) {
-            bo = bo_n;
-            bq = bq_n;
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      };
-      (void)need_mask;
-      step(std::true_type{});
+      for (int nb = 0; nb < 2; ++nb) {
+        mma_a(dv[nb][db], pa[nb][1], bo);
+        mma_a(dk[nb][db], da[nb][1], bq);
+      }
+      if (db + 1 < NDB) {
+        bo = bo_n;
+        bq = bq_n;
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   int cb = 0;  // buffer of step s
+  int it = i_first;
   for (int s = 0; s < total; ++s) {
     const int nb2 = cb >= 1 ? cb - 1 : 2;  // (s + 2) % 3
-    step_body(smem + cb * C::BUF, vrows, smem + nb2 * C::BUF, s);
+    step_body(smem + cb * C::BUF, vrows, smem + nb2 * C::BUF, it * BM);
     // tile s + 1 must have landed; the loads of tile s + 2 may stay in flight
-    if (s + 2 < total) wait_vm_le<C::ISSUE_MIN>();
-    else wait_vm_all();
+    wait_vm_le<C::ISSUE>();
     barrier_lds();
     cb = cb == 2 ? 0 : cb + 1;
+    if (++it == n_qt) it = i_first;
   }
+  // the epilogue reuses the staging buffers: every prefetch must have landed
+  wait_vm_all();
+  barrier_lds();
 
   mma_drain(dk[0]);
   mma_drain(dk[1]);
@@ -375,12 +390,14 @@ struct Dq16 {
   typedef TileLayout<HD> L;
   static constexpr int BM = 256, BN = 32;
   static constexpr int RB = L::RB;
-  static constexpr int GPR = L::GPR;
   static constexpr int TILE = (BN * RB + 1023) / 1024 * 1024;  // one K or V tile (whole KB)
   static constexpr int BUF = 2 * TILE;
   static constexpr int STAGES = 3;
-  static constexpr int LDS = STAGES * BUF;
-  static constexpr int ISSUE_MIN = 2 * tile_loads_min<HD, BN>(4);
+  static constexpr int SPARE = 1024;  // target of the padding loads (never read)
+  static constexpr int LDS = STAGES * BUF + SPARE;
+  typedef TileDma<bf16, HD, BN> Dma;  // (the element type only sets the row size)
+  static constexpr int KMAX = Dma::KMAX;
+  static constexpr int ISSUE = 2 * KMAX;  // loads each wave issues per stage
 };
 
 template <class T, int HD>
@@ -391,6 +408,7 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
   constexpr int BM = C::BM, BN = C::BN, RB = C::RB;
 
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+  char* const spare = smem + C::STAGES * C::BUF;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
@@ -454,27 +472,31 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
   const int n_kt = (Sk + BN - 1) / BN;
   const int j_end = causal ? min(n_kt, (min(m0 + BM, Sq) - 1) / BN + 1) : n_kt;
 
+  // K and V tiles of the kv head through buffer resources: a tile is selected by a uniform
+  // byte offset, keys past Sk read as zeros (and are masked), and the prefetches issued past
+  // the last tile land in stages nothing reads any more.
   TileDma<T, HD, BN> kvdma;
   kvdma.init(w, lane);
+  const rsrc_t rk = make_rsrc(Kg, (unsigned)((size_t)Sk * HD * sizeof(T)));
+  const rsrc_t rv = make_rsrc(Vg, (unsigned)((size_t)Sk * HD * sizeof(T)));
+  constexpr unsigned TILEB = BN * HD * sizeof(T);  // source bytes of one key tile
   auto issue_part = [&](int j, char* buf, int k) {
-    const bool full = (j + 1) * BN <= Sk;
-    kvdma.issue(k, buf, Kg, j * BN, Sk - 1, full);
-    kvdma.issue(k, buf + C::TILE, Vg, j * BN, Sk - 1, full);
+    kvdma.issue(k, buf, rk, (unsigned)j * TILEB, spare);
+    kvdma.issue(k, buf + C::TILE, rv, (unsigned)j * TILEB, spare);
   };
   auto issue = [&](int j, char* buf) {
 #pragma unroll
-    for (int k = 0; k < TileDma<T, HD, BN>::KMAX; ++k) issue_part(j, buf, k);
+    for (int k = 0; k < C::KMAX; ++k) issue_part(j, buf, k);
   };
 
-  issue(0, smem);  // j_end >= 1 always
-  if (j_end > 1) issue(1, smem + C::BUF);
-  if (j_end > 1) wait_vm_le<C::ISSUE_MIN>();
-  else wait_vm_all();
-  __syncthreads();
+  issue(0, smem);
+  issue(1, smem + C::BUF);
+  wait_vm_le<C::ISSUE>();  // Q, dO, statistics and stage 0 have landed
+  barrier_lds();
+  const float mask_s = p.mask_s;
 
   // One step; restrict pointers as in the dK/dV kernel.
   auto step_body = [&](const char* __restrict__ cur, char* __restrict__ nxt, int j) {
-    const bool pf = j + 2 < j_end;
     const int n0 = j * BN;
     {
       f32x16 St[2], dPt[2];
@@ -487,7 +509,7 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
       for (int cc = 0; cc < NC; ++cc) {
         const F ak = lds_frag<T>(cur, a_off[cc]);
         const F av = lds_frag<T>(cur + C::TILE, a_off[cc]);
-        if (pf && cc < TileDma<T, HD, BN>::KMAX) issue_part(j + 2, nxt, cc);
+        if (cc < C::KMAX) issue_part(j + 2, nxt, cc);
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
           mma(St[mb], ak, qf[mb][cc]);
@@ -497,19 +519,24 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
       F da[2][2];
-      // Register r of this lane holds key n0 + 4 hl + off(r), off = 8 (r / 4) + r % 4; it may
-      // be seen iff off < lim[mb] = min(Sk, causal ? m + 1 : Sk) - n0 - 4 hl.  Applied on every
-      // step (one compare and select per element) so the loop body has a single path.
-      int lim[2];
+      // Masking, only on steps that need it (the causal diagonal, the last key tile): a cut
+      // score is replaced by mask_s, whose exponent is -inf.  Register r of this lane holds
+      // key n0 + 4 hl + off(r), off = 8 (r / 4) + r % 4, of row m (one row per lane); it may be
+      // seen iff off < min(Sk, causal ? m + 1 : Sk) - n0 - 4 hl.
+      if ((n0 + BN > Sk) || (causal && n0 + BN - 1 > mw0)) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int m = mw0 + 32 * mb + c32;
-        lim[mb] = (causal ? min(Sk, m + 1) : Sk) - n0 - 4 * hl;
+        for (int mb = 0; mb < 2; ++mb) {
+          const int m = mw0 + 32 * mb + c32;
+          const int lim = (causal ? min(Sk, m + 1) : Sk) - n0 - 4 * hl;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = 8 * (r >> 2) + (r & 3);
+            St[mb][r] = off < lim ? St[mb][r] : mask_s;
+          }
+        }
       }
       auto elem = [&](int mb, int r) {
-        float pv = fast_exp2(St[mb][r] * p.scale_log2 - lse2[mb]);
-        const int off = 8 * (r >> 2) + (r & 3);
-        pv = off < lim[mb] ? pv : 0.f;
+        const float pv = fast_exp2(St[mb][r] * p.scale_log2 - lse2[mb]);
         da[mb][r >> 3][r & 7] = (T)(pv * (dPt[mb][r] - dl[mb]));
       };
 #pragma unroll
@@ -551,11 +578,11 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
   for (int j = 0; j < j_end; ++j) {
     const int nb2 = cb >= 1 ? cb - 1 : 2;
     step_body(smem + cb * C::BUF, smem + nb2 * C::BUF, j);
-    if (j + 2 < j_end) wait_vm_le<C::ISSUE_MIN>();
-    else wait_vm_all();
+    wait_vm_le<C::ISSUE>();  // tile j + 1 has landed; tile j + 2 may stay in flight
     barrier_lds();
     cb = cb == 2 ? 0 : cb + 1;
   }
+  wait_vm_all();  // no prefetch may still be writing LDS when the workgroup ends
 
   mma_drain(dq[0]);
   mma_drain(dq[1]);

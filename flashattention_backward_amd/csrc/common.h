@@ -187,73 +187,82 @@ __device__ __forceinline__ typename Frag<T>::type lds_frag_tr(const char* base, 
   return __builtin_bit_cast(typename Frag<T>::type, v);
 }
 
-// 16 bytes from global memory straight into LDS (global_load_lds_dwordx4): lane l of the wave
-// writes lds_wave_base + 16 * l.  lds_wave_base must be the same for the whole wave.
-__device__ __forceinline__ void g2lds16(const void* src, char* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_char*)lds_wave_base, 16, 0, 0);
+// Direct global->LDS copies use buffer loads with the LDS bit (buffer_load_dwordx4 ... lds):
+// lane l of the wave writes 16 bytes at lds_wave_base + 16 * l, read from byte offset
+// voff + soff of a raw buffer resource.  The buffer form (rather than global_load_lds) keeps
+// the compiler's LDS wait counting exact: a flat-encoded load that also writes LDS makes
+// every later LDS wait drain to zero while it is in flight, and the prefetch here is in
+// flight across whole compute steps.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw (unstrided) buffer resource over `bytes` bytes from `base`; dword 3 is the gfx9
+// default (32-bit data format, no swizzle).  Reads at offsets >= bytes return zero.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Copy rows [row0, row0 + ROWS) of a row-major [*, HD] tensor into an LDS tile in
-// TileLayout<HD>, with direct global->LDS loads spread over `nw` waves (this one is wave w).
-// Rows past `last_row` are loaded from `last_row` (finite data; callers mask them).
+__device__ __forceinline__ void b2lds16(rsrc_t r, unsigned voff, unsigned soff, char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_char*)lds_wave_base,
+                                           16, voff, soff, 0, 0);
+}
+
+// Copy rows [row0, row0 + ROWS) of a row-major [*, HD] tensor slice (rows 0 .. last_row,
+// starting at `src`) into an LDS tile in TileLayout<HD>, with direct loads spread over `nw`
+// waves (this one is wave w).  Rows past `last_row` are loaded from `last_row` (finite data;
+// callers mask them).
 template <class T, int HD, int ROWS>
 __device__ __forceinline__ void load_tile(char* tile, const T* src, int row0, int last_row,
                                           int w, int nw, int lane) {
   typedef TileLayout<HD> L;
   constexpr int NG = ROWS * L::GPR;      // granules in the tile
   constexpr int NI = (NG + 63) / 64;     // wave instructions (1 KB each)
+  const rsrc_t r = make_rsrc(src, (unsigned)(last_row + 1) * HD * sizeof(T));
 #pragma unroll
   for (int k = 0; k < (NI + 3) / 4; ++k) {
     const int q = w + nw * k;
     if (q < NI) {
       const int gi = 64 * q + lane;
       if (NG % 64 == 0 || gi < NG) {
-        const int r = gi / L::GPR, pc = gi % L::GPR;
-        const int row = min(row0 + r, last_row);
-        g2lds16(src + (size_t)row * HD + 8 * L::chunk_at(r, pc), tile + 1024 * q);
+        const int rr = gi / L::GPR, pc = gi % L::GPR;
+        const int row = min(row0 + rr, last_row);
+        b2lds16(r, (unsigned)((row * HD + 8 * L::chunk_at(rr, pc)) * sizeof(T)), 0u, tile + 1024 * q);
       }
     }
   }
 }
 
 // The same copy split into single instructions, so that a prefetch can be spread over a
-// compute step instead of stalling the wave's issue at one point.  Per-lane granule offsets
-// (element offset of the granule within the tile's source rows) are computed once.
+// compute step instead of stalling the wave's issue at one point.  The source is a buffer
+// resource over whole rows; the tile's first row is selected by a uniform byte offset
+// (soffset), so each instruction needs no per-lane address arithmetic.  Rows past the end
+// of the resource read as zeros.  Every wave issues KMAX instructions: where the tile has no
+// instruction left for a wave, it writes to `spare` (1 KB of LDS nothing reads), which keeps
+// the per-wave load count uniform for the vmcnt waits and the issue free of branches.  The
+// last instruction of a tile may cover fewer granules than lanes; the extra lanes write into
+// the tile's rounding slack (tiles are rounded up to whole KB).
 template <class T, int HD, int ROWS>
 struct TileDma {
   typedef TileLayout<HD> L;
   static constexpr int NG = ROWS * L::GPR;
   static constexpr int NI = (NG + 63) / 64;   // wave instructions for the whole tile
-  static constexpr int KMAX = (NI + 3) / 4;   // most instructions any of 4 waves issues
+  static constexpr int KMAX = (NI + 3) / 4;   // instructions each of 4 waves issues
+  static constexpr unsigned ROWB = HD * sizeof(T);  // bytes per source row
+  static_assert(NG % 64 == 0 || (NG % 64) * 16 + (NI - 1) * 1024 <= NI * 1024, "slack");
   int w;
-  unsigned src_off[KMAX];  // r * HD + 8 * chunk for this lane's granule of instruction k
-  int row_of[KMAX];        // tile row of that granule
-  bool valid[KMAX];        // this lane's granule exists (last instruction may be partial)
+  unsigned src_off[KMAX];  // byte offset of this lane's granule of instruction k from row 0
   __device__ __forceinline__ void init(int wave, int lane) {
     w = wave;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
       const int gi = 64 * (w + 4 * k) + lane;
       const int r = gi / L::GPR, pc = gi % L::GPR;
-      row_of[k] = r;
-      valid[k] = gi < NG;
-      src_off[k] = (unsigned)(r * HD + 8 * L::chunk_at(r, pc));
+      src_off[k] = (unsigned)r * ROWB + (unsigned)(8 * L::chunk_at(r, pc) * sizeof(T));
     }
   }
-  __device__ __forceinline__ bool has(int k) const { return w + 4 * k < NI; }
-  // Instruction k of this wave: rows row0 .. row0 + ROWS - 1 of src into `tile`; rows past
-  // last_row are read from last_row.  `full` (uniform): no row needs clamping.
-  __device__ __forceinline__ void issue(int k, char* tile, const T* src, int row0, int last_row,
-                                        bool full) const {
-    if (!has(k)) return;
-    char* dst = tile + 1024 * (w + 4 * k);
-    if (NG % 64 != 0 && !valid[k]) return;
-    if (full) {
-      g2lds16(src + (size_t)row0 * HD + src_off[k], dst);
-    } else {
-      const int row = min(row0 + row_of[k], last_row);
-      g2lds16(src + (size_t)row * HD + (src_off[k] - (unsigned)(row_of[k] * HD)), dst);
-    }
+  // Instruction k of this wave: the tile whose first row starts at byte `soff` of `r`.
+  __device__ __forceinline__ void issue(int k, char* tile, rsrc_t r, unsigned soff, char* spare) const {
+    char* dst = (w + 4 * k < NI) ? tile + 1024 * (w + 4 * k) : spare;
+    b2lds16(r, src_off[k], soff, dst);
   }
 };
 
@@ -278,11 +287,7 @@ __device__ __forceinline__ void wait_vm_le() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Fewest direct-load instructions any of `nw` waves issues for a tile of ROWS rows.
-template <int HD, int ROWS>
-constexpr int tile_loads_min(int nw) {
-  return ((ROWS * TileLayout<HD>::GPR + 63) / 64) / nw;
-}
+
 
 // Work-item mapping shared by the launches: workgroup ids are dispatched round-robin over
 // the 8 XCDs, so id w runs on XCD w % 8.  When the independent units (kv-head groups) split

@@ -49,7 +49,8 @@ struct BwdParams {
   int B, H, H_kv, Sq, Sk, Sq_pad;
   int causal;
   float scale;
-  float scale_log2;
+  float scale_log2;  // scale * log2(e), never zero or subnormal
+  float mask_s;      // a score replaced by mask_s gets exponent mask_s * scale_log2 = -inf
   int n_units;
   int units_per_xcd;
 };

@@ -53,6 +53,21 @@ def test_shapes_and_edges(fab, shape):
     check_end_to_end(fab, w)
 
 
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 1e-3, 0.5])
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("fp16", 64)])
+def test_scale_values(fab, dt, D, scale):
+    """Softmax scales of either sign, zero and tiny: a masked score is replaced by a value
+    whose exponent is -inf for the sign of the scale, and a zero scale runs with the smallest
+    normal exponent scale.  Causal, with ragged tails, so masked steps are exercised."""
+    w = workloads.Workload(f"scale_{dt}", dt, 1, 4, 2, 150, 170, D, True, seed=31)
+    say(f"[case] scale={scale} {dt} D={D}")
+    q, k, v, do = workloads.make_inputs(w)
+    out = run_gpu(fab, q, k, v, do, True, scale)
+    ref = oracle.attention_grads(q, k, v, do, True, scale)
+    for name in ("o", "lse", "dq", "dk", "dv"):
+        assert_close(name, to_np64(out[name]), ref[name], "fp32" if name == "lse" else dt)
+
+
 @pytest.mark.parametrize("dt", ["bf16", "fp16", "fp32"])
 def test_isolated_backward(fab, dt):
     """Diagnostic mode: the GPU backward fed the oracle's O (rounded to the dtype) and LSE."""
