@@ -174,10 +174,22 @@ class Bwd:
                                    self.dq.data_ptr(), *self.dims, self.stream))
 
 
+def settle(fn, seconds=0.3):
+    """Untimed calls of fn() until the GPU has been busy for about `seconds`, so that the
+    timed region starts at the steady clock rather than during the clock ramp."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+
+
 def time_launches(fn, steps, warmup):
     """Average milliseconds per call of fn() over `steps` calls, timed with events recorded
     on the stream the library launches on (torch's current stream)."""
     import torch
+    settle(fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -197,6 +209,7 @@ def bench_workload(w, steps, warmup, with_cpu, inputs=None):
     cpu = cpu_baseline(w, q, k, v, do) if with_cpu else None
     b = Bwd(w, q, k, v, do)
     torch.cuda.synchronize()
+    settle(b.bwd)
     # the timed region: `steps` whole backward calls, synchronised on both sides
     for _ in range(warmup):
         b.bwd()

@@ -31,21 +31,21 @@ template <int HD>
 struct Dkdv16 {
   typedef TileLayout<HD> L;
   static constexpr int BN = 128, BM = 64;
-  static constexpr int RB = L::RB;             // bytes per tile row
-  static constexpr int TILE = (BM * RB + 1023) / 1024 * 1024;  // one Q or dO tile (whole KB)
+  static constexpr int TILE = L::bytes(BM);    // one Q or dO tile
   static constexpr int STATS = 1024;           // {lse2, D} of 128 rows (one wave-wide load)
   static constexpr int BUF = 2 * TILE + STATS; // one stage: Q, dO, stats
-  static constexpr int VT = (BN * RB + 1023) / 1024 * 1024;  // V tile of the workgroup
+  static constexpr int VT = L::bytes(BN);      // V tile of the workgroup
   static constexpr int STAGES = 3;             // tiles in flight: current + 2 prefetched
-  static constexpr int SPARE = 1024;           // target of the padding loads (never read)
-  static constexpr int LDS = STAGES * BUF + VT + SPARE;
-  static constexpr int RED = 2 * 64 * HD * 4;  // epilogue: two waves' partial dK or dV
   typedef TileDma<bf16, HD, BM> Dma;           // (the element type only sets the row size)
   static constexpr int KMAX = Dma::KMAX;
+  static constexpr int SPARE = Dma::kSpare ? 1024 : 0;  // target of padding loads
+  static constexpr int LDS = STAGES * BUF + VT + SPARE;
+  static constexpr int RED = 2 * 64 * HD * 4;  // epilogue: two waves' partial dK or dV
   // Loads each wave issues per stage (Q and dO; wave 0 adds the statistics).
   static constexpr int ISSUE = 2 * KMAX;
   static_assert(RED <= LDS, "reduction must fit in the staging buffers");
   static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert(TILE % 16 == 0 && VT % 16 == 0, "granule alignment");
 };
 
 template <class T, int HD>
@@ -54,12 +54,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   typedef typename Frag<T>::type F;
   typedef TileDma<T, HD, Dkdv16<HD>::BM> Dma;
   constexpr int NC = HD / 16, NDB = HD / 32;
-  constexpr int BM = C::BM, BN = C::BN, RB = C::RB;
+  constexpr int BM = C::BM, BN = C::BN;
+  typedef typename C::L L;
   constexpr unsigned ROWB = HD * sizeof(T);
 
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
   char* const vtile = smem + C::STAGES * C::BUF;
-  char* const spare = vtile + C::VT;
+  char* const spare = vtile + C::VT;  // only used when the tile DMA needs padding loads
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   // A operand (Q or dO rows): row 32 qh + c32, chunk 2 cc + hl
   int a_off[NC];
 #pragma unroll
-  for (int cc = 0; cc < NC; ++cc) a_off[cc] = C::L::off(32 * qh + c32, 2 * cc + hl);
+  for (int cc = 0; cc < NC; ++cc) a_off[cc] = L::off(32 * qh + c32, 2 * cc + hl);
   // B operand of P^T dO / dS^T Q, transposed read: 16-lane group (hl, dh), lane i in group
   const int gi16 = lane & 15, dh = (lane >> 4) & 1;
   int t_off[NDB][2];
@@ -110,14 +111,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
     for (int sec = 0; sec < 2; ++sec) {
       const int r = 32 * qh + 4 * hl + 8 * sec + (gi16 >> 2);
       const int col = 32 * db + 16 * dh + 4 * (gi16 & 3);
-      t_off[db][sec] = C::L::off(r, col >> 3) + 2 * (col & 7);
+      t_off[db][sec] = L::off(r, col >> 3) + 2 * (col & 7);
     }
   // B operand of dP = dO V^T: V rows 64 kb + 32 nb + c32 have the same layout offsets as the
-  // A operand rows 32 qh + c32 (both are c32 mod 16), so they are a_off plus a wave constant.
-  const char* const vrows = vtile + (64 * kb - 32 * qh) * RB;
+  // A operand rows 32 qh + c32 shifted by a whole number of row groups, so they are a_off
+  // plus a wave constant.
+  const char* const vrows = vtile + L::rows(64 * kb) - L::rows(32 * qh);
 
   // ---- iteration space: every query head of the group and every query tile whose rows
-  // the causal mask lets reach these keys; step s is head s / per, tile i_first + s % per.
+  // the causal mask lets reach these keys.  Tiles run from the last one down, heads inside:
+  // step s is tile n_qt - 1 - s / G of head s % G.  Every key tile's sequence starts at the
+  // same (tile, head), so the workgroups of a group that run together on an XCD read the
+  // same Q and dO tile at about the same time and share it through that XCD's L2.
   const int n_qt = (Sq + BM - 1) / BM;
   const int i_first = causal ? min(n0 / BM, n_qt) : 0;
   const int per = n_qt - i_first;
@@ -136,19 +141,21 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
 
   Dma qdma;
   qdma.init(w, lane);
-  // Head and tile of the next stage to prefetch, advanced once per issued stage.
-  int ph = 0, pit = i_first;
+  // Head and tile of the next stage to prefetch, advanced once per issued stage.  Past the
+  // last step the offsets leave the group (or wrap): those reads are range-checked zeros or
+  // in-range rows, landing in a stage nothing reads.
+  int ph = 0, pit = n_qt - 1;
   auto issue_part = [&](char* buf, int k, unsigned q_soff, unsigned st_soff) {
-    qdma.issue(k, buf, rq, q_soff, spare);
-    qdma.issue(k, buf + C::TILE, rdo, q_soff, spare);
+    qdma.issue(k, buf, rq, q_soff, spare, lane);
+    qdma.issue(k, buf + C::TILE, rdo, q_soff, spare, lane);
     if (k == 0 && w == 0) b2lds16(rst, 16u * lane, st_soff, buf + 2 * C::TILE);
   };
   auto next_offsets = [&](unsigned& q_soff, unsigned& st_soff) {
     q_soff = (unsigned)(ph * Sq + pit * BM) * ROWB;
     st_soff = (unsigned)(ph * Sq_pad + pit * BM) * 8u;
-    if (++pit == n_qt) {
-      pit = i_first;
-      ++ph;
+    if (++ph == G) {
+      ph = 0;
+      --pit;
     }
   };
   auto issue = [&](char* buf) {
@@ -170,52 +177,72 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   // One step.  The stage being read, the resident V tile and the stage being prefetched are
   // passed as restrict pointers: the compiler then knows that the direct-to-LDS prefetch does
   // not write what this step reads, and does not make the step's LDS reads wait for it.
+  //
+  // The step is ordered so that the matrix cores always have work while the vector ALU
+  // computes the softmax: S first; then dP, with the exponentials of P (which need only S)
+  // computed while its MFMAs run; then dV += P^T dO for the first 16 rows while dS of those
+  // rows is formed; dK += dS^T Q for them while dS of the other 16 rows is formed; and last
+  // both products for the second 16 rows.
+  // Operands that open a step: the Q fragments of every head-dim slice and the statistics of
+  // this lane's 16 rows (register r of a block holds row m_base + off(r), off(r) = 8 (r / 4) +
+  // r % 4).  They are read from the stage of the next step while the current step's last
+  // MFMAs run, so a step starts with them in registers.
+  F aq[NC];
+  float l2[16], dl[16];
+  auto load_step_operands = [&](const char* __restrict__ buf) {
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) aq[cc] = lds_frag<T>(buf, a_off[cc]);
+    const float* st = reinterpret_cast<const float*>(buf + 2 * C::TILE);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ml = 32 * qh + 8 * j + 4 * hl;
+      const f32x4 s01 = *reinterpret_cast<const f32x4*>(st + 2 * ml);
+      const f32x4 s23 = *reinterpret_cast<const f32x4*>(st + 2 * ml + 4);
+      l2[4 * j + 0] = s01[0]; dl[4 * j + 0] = s01[1];
+      l2[4 * j + 1] = s01[2]; dl[4 * j + 1] = s01[3];
+      l2[4 * j + 2] = s23[0]; dl[4 * j + 2] = s23[1];
+      l2[4 * j + 3] = s23[2]; dl[4 * j + 3] = s23[3];
+    }
+  };
+  load_step_operands(smem);
+
+  // One step on stage `cur`; `nb1` is the stage of the next step and `nxt` the stage being
+  // prefetched (step s + 2).  The workgroup barrier that ends the step sits before its last
+  // eight MFMAs: by then every read of `cur` has completed, and the next step's operands are
+  // read from `nb1` while those MFMAs run.
   auto step_body = [&](const char* __restrict__ cur, const char* __restrict__ vrows,
-                       char* __restrict__ nxt, int m0) {
-    // The prefetch of step s + 2 is issued one instruction per head-dim slice of the first
-    // contraction, so the wave never stalls on a burst of memory instructions.
+                       char* __restrict__ nxt, const char* __restrict__ nb1, int m0) {
     unsigned pq_soff, pst_soff;
     next_offsets(pq_soff, pst_soff);
     const int mw0 = m0 + 32 * qh;
+
+    // ---- S = Q K^T for both key blocks; the prefetch of step s + 2 is spread over it, one
+    // instruction per head-dim slice, so the wave never stalls on a burst of loads.
     f32x16 S[2], dP[2];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      S[nb] = f32x16{};
-      dP[nb] = f32x16{};
-    }
-    // Operands of slice cc + 1 are read while the MFMAs of slice cc run.
-    F aq = lds_frag<T>(cur, a_off[0]);
-    F ad = lds_frag<T>(cur + C::TILE, a_off[0]);
-    F bv0 = lds_frag<T>(vrows, a_off[0]);
-    F bv1 = lds_frag<T>(vrows + 32 * RB, a_off[0]);
+    for (int nb = 0; nb < 2; ++nb) S[nb] = f32x16{};
+    // Operands of dP = dO V^T stream through a window LEAD head-dim slices deep; the first
+    // LEAD slices are read here, under the S MFMAs (LDS latency under load is several MFMAs).
+    constexpr int LEAD = NC >= 8 ? 3 : 2;
+    F ad[NC], bv0[NC], bv1[NC];
+    auto read_dp_operands = [&](int cc) {
+      ad[cc] = lds_frag<T>(cur + C::TILE, a_off[cc]);
+      bv0[cc] = lds_frag<T>(vrows, a_off[cc]);
+      bv1[cc] = lds_frag<T>(vrows + L::rows(32), a_off[cc]);
+    };
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
-      F aq_n, ad_n, bv0_n, bv1_n;
-      if (cc + 1 < NC) {
-        aq_n = lds_frag<T>(cur, a_off[cc + 1]);
-        ad_n = lds_frag<T>(cur + C::TILE, a_off[cc + 1]);
-        bv0_n = lds_frag<T>(vrows, a_off[cc + 1]);
-        bv1_n = lds_frag<T>(vrows + 32 * RB, a_off[cc + 1]);
-      }
       if (cc < C::KMAX) issue_part(nxt, cc, pq_soff, pst_soff);
-      mma(S[0], aq, kf[0][cc]);
-      mma(dP[0], ad, bv0);
-      mma(S[1], aq, kf[1][cc]);
-      mma(dP[1], ad, bv1);
-      if (cc + 1 < NC) {
-        aq = aq_n;
-        ad = ad_n;
-        bv0 = bv0_n;
-        bv1 = bv1_n;
-      }
+      if (cc < LEAD) read_dp_operands(cc);
+      mma(S[0], aq[cc], kf[0][cc]);
+      mma(S[1], aq[cc], kf[1][cc]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
 
     // Masking, only on steps that need it (the causal diagonal, the last key tile): a cut
     // score is replaced by mask_s, whose exponent is -inf, so P = 0 and dS = 0 there.  Key n
     // (this lane's column of block nb) may be seen by row m iff n < Sk and (not causal or
-    // n <= m); register r holds row m_base + off(r), off(r) = 8 (r / 4) + r % 4.
+    // n <= m).
     if ((n0 + BN > Sk) || (causal && nw0 + 63 > mw0)) {
       const int m_base = mw0 + 4 * hl;
 #pragma unroll
@@ -230,99 +257,114 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
       }
     }
 
-    const float* st = reinterpret_cast<const float*>(cur + 2 * C::TILE);
-    // P and dS go straight into the 16-bit operand fragments of the next contractions:
-    // fragment (nb, ks) holds accumulator registers 8 ks .. 8 ks + 7 of block nb.
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- dP = dO V^T, with P = exp2(S scale log2e - lse2) computed in place of S (and its
+    // 16-bit copy, the A operand of dV += P^T dO) while the MFMAs run.  Fragment (nb, ks)
+    // holds registers 8 ks .. 8 ks + 7 of block nb.  The dP MFMAs are volatile asm and every
+    // exponential is pinned between them with order_point(), so the interleave is exact.
     F pa[2][2], da[2][2];
-    // Row statistics for registers 8 ks .. 8 ks + 7 (rows m_base + 8 j + e, j = 2 ks, 2 ks + 1).
-    auto load_stats = [&](int ks, float (&l2)[8], float (&dl)[8]) {
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int ml = 32 * qh + 8 * (2 * ks + jj) + 4 * hl;
-        const f32x4 s01 = *reinterpret_cast<const f32x4*>(st + 2 * ml);
-        const f32x4 s23 = *reinterpret_cast<const f32x4*>(st + 2 * ml + 4);
-        l2[4 * jj + 0] = s01[0]; dl[4 * jj + 0] = s01[1];
-        l2[4 * jj + 1] = s01[2]; dl[4 * jj + 1] = s01[3];
-        l2[4 * jj + 2] = s23[0]; dl[4 * jj + 2] = s23[1];
-        l2[4 * jj + 3] = s23[2]; dl[4 * jj + 3] = s23[3];
-      }
+    constexpr int PER_CC = 32 / NC;  // exponentials per head-dim slice
+    auto pexp = [&](int e) {
+      const int nb = e >> 4, r = e & 15;
+      float x = fast_exp2(S[nb][r] * p.scale_log2 - l2[r]);
+      order_point(x);
+      S[nb][r] = x;
+      pa[nb][r >> 3][r & 7] = (T)x;
     };
-    // One element: register r = 8 ks + t of block nb.
-    auto elem = [&](int nb, int ks, int t, const float (&l2)[8], const float (&dl)[8]) {
-      const int r = 8 * ks + t;
-      const float pv = fast_exp2(S[nb][r] * p.scale_log2 - l2[t]);
-      pa[nb][ks][t] = (T)pv;
-      da[nb][ks][t] = (T)(pv * (dP[nb][r] - dl[t]));
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      if (cc + LEAD < NC) read_dp_operands(cc + LEAD);
+      if (cc == 0) mma_v0(dP[0], ad[cc], bv0[cc]);
+      else mma_v(dP[0], ad[cc], bv0[cc]);
+#pragma unroll
+      for (int k = 0; k < PER_CC / 2; ++k) pexp(cc * PER_CC + k);
+      if (cc == 0) mma_v0(dP[1], ad[cc], bv1[cc]);
+      else mma_v(dP[1], ad[cc], bv1[cc]);
+#pragma unroll
+      for (int k = PER_CC / 2; k < PER_CC; ++k) pexp(cc * PER_CC + k);
+    }
+    mma_vdrain(dP);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // dS = P (dP - D) for register r of block nb, into its 16-bit fragment.
+    auto ds = [&](int nb, int r) {
+      da[nb][r >> 3][r & 7] = (T)(S[nb][r] * (dP[nb][r] - dl[r]));
     };
-    // dV += P^T dO and dK += dS^T Q for one 16-row slice ks of the query rows.  While the
-    // 16 MFMAs of slice 0 run, the softmax of slice 1 (16 elements) is interleaved with them.
-    float l2[8], dl[8];
-    load_stats(0, l2, dl);
+    // B operands, transposed reads of the dO and Q tiles: d block db, row slice ks.
+    auto b_do = [&](int db, int ks) {
+      return lds_frag_tr<T>(cur + C::TILE, t_off[db][0] + L::rows(16) * ks, t_off[db][1] + L::rows(16) * ks);
+    };
+    auto b_q = [&](int db, int ks) {
+      return lds_frag_tr<T>(cur, t_off[db][0] + L::rows(16) * ks, t_off[db][1] + L::rows(16) * ks);
+    };
+
+    // ---- dV += P^T dO, rows 0..15 of the wave, with dS of those rows formed meanwhile.
+    F bo[NDB], bq[NDB];
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) elem(nb, 0, t, l2, dl);
-    load_stats(1, l2, dl);
-    // Slice 0 MFMAs with the slice 1 softmax woven in; the B operands of the next d block
-    // are read one block ahead.  Scheduling fences keep the compiler from hoisting every
-    // LDS read to the top (which would not fit in the register file).
-    F bo = lds_frag_tr<T>(cur + C::TILE, t_off[0][0], t_off[0][1]);
-    F bq = lds_frag_tr<T>(cur, t_off[0][0], t_off[0][1]);
+    for (int db = 0; db < NDB; ++db) bo[db] = b_do(db, 0);
+    constexpr int PER_MMA = 16 / (2 * NDB);  // dS elements per MFMA of a 16-row slice
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      F bo_n, bq_n;
-      if (db + 1 < NDB) {
-        bo_n = lds_frag_tr<T>(cur + C::TILE, t_off[db + 1][0], t_off[db + 1][1]);
-        bq_n = lds_frag_tr<T>(cur, t_off[db + 1][0], t_off[db + 1][1]);
-      } else {
-        bo_n = lds_frag_tr<T>(cur + C::TILE, t_off[0][0] + 16 * RB, t_off[0][1] + 16 * RB);
-        bq_n = lds_frag_tr<T>(cur, t_off[0][0] + 16 * RB, t_off[0][1] + 16 * RB);
-      }
+      bq[db] = b_q(db, 0);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        constexpr int per_db = 16 / NDB;  // slice-1 elements per d block
-        mma_a(dv[nb][db], pa[nb][0], bo);
+        mma_a(dv[nb][db], pa[nb][0], bo[db]);
 #pragma unroll
-        for (int k = 0; k < per_db / 2; ++k) {
-          const int e = db * per_db + nb * (per_db / 2) + k;
-          elem(e & 1, 1, e >> 1, l2, dl);
+        for (int k = 0; k < PER_MMA; ++k) {
+          const int e = (2 * db + nb) * PER_MMA + k;  // 0..15 over rows 0..15 of both blocks
+          ds(e & 1, e >> 1);
         }
-        mma_a(dk[nb][db], da[nb][0], bq);
       }
-      bo = bo_n;
-      bq = bq_n;
       __builtin_amdgcn_sched_barrier(0);
     }
+    // ---- dK += dS^T Q, rows 0..15, with dS of rows 16..31 formed meanwhile.
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      F bo_n, bq_n;
-      if (db + 1 < NDB) {
-        bo_n = lds_frag_tr<T>(cur + C::TILE, t_off[db + 1][0] + 16 * RB, t_off[db + 1][1] + 16 * RB);
-        bq_n = lds_frag_tr<T>(cur, t_off[db + 1][0] + 16 * RB, t_off[db + 1][1] + 16 * RB);
-      }
+      bo[db] = b_do(db, 1);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        mma_a(dv[nb][db], pa[nb][1], bo);
-        mma_a(dk[nb][db], da[nb][1], bq);
+        mma_a(dk[nb][db], da[nb][0], bq[db]);
+#pragma unroll
+        for (int k = 0; k < PER_MMA; ++k) {
+          const int e = (2 * db + nb) * PER_MMA + k;
+          ds(e & 1, 8 + (e >> 1));
+        }
       }
-      if (db + 1 < NDB) {
-        bo = bo_n;
-        bq = bq_n;
-      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // ---- dV += P^T dO for rows 16..31, reading the last B operands of this stage.
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      bq[db] = b_q(db, 1);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) mma_a(dv[nb][db], pa[nb][1], bo[db]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // ---- end of the step for the workgroup: the next stage has landed (the loads of the one
+    // after it may stay in flight) and no wave reads `cur` any more.
+    wait_vm_le<C::ISSUE>();
+    barrier_lds();
+    load_step_operands(nb1);
+    // ---- dK += dS^T Q for rows 16..31 while the next step's operands arrive.
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) mma_a(dk[nb][db], da[nb][1], bq[db]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   int cb = 0;  // buffer of step s
-  int it = i_first;
+  int it = n_qt - 1, hh = 0;
   for (int s = 0; s < total; ++s) {
+    const int nb1 = cb == 2 ? 0 : cb + 1;  // (s + 1) % 3
     const int nb2 = cb >= 1 ? cb - 1 : 2;  // (s + 2) % 3
-    step_body(smem + cb * C::BUF, vrows, smem + nb2 * C::BUF, it * BM);
-    // tile s + 1 must have landed; the loads of tile s + 2 may stay in flight
-    wait_vm_le<C::ISSUE>();
-    barrier_lds();
-    cb = cb == 2 ? 0 : cb + 1;
-    if (++it == n_qt) it = i_first;
+    step_body(smem + cb * C::BUF, vrows, smem + nb2 * C::BUF, smem + nb1 * C::BUF, it * BM);
+    cb = nb1;
+    if (++hh == G) {
+      hh = 0;
+      --it;
+    }
   }
   // the epilogue reuses the staging buffers: every prefetch must have landed
   wait_vm_all();
@@ -389,14 +431,13 @@ template <int HD>
 struct Dq16 {
   typedef TileLayout<HD> L;
   static constexpr int BM = 256, BN = 32;
-  static constexpr int RB = L::RB;
-  static constexpr int TILE = (BN * RB + 1023) / 1024 * 1024;  // one K or V tile (whole KB)
+  static constexpr int TILE = L::bytes(BN);  // one K or V tile
   static constexpr int BUF = 2 * TILE;
   static constexpr int STAGES = 3;
-  static constexpr int SPARE = 1024;  // target of the padding loads (never read)
-  static constexpr int LDS = STAGES * BUF + SPARE;
   typedef TileDma<bf16, HD, BN> Dma;  // (the element type only sets the row size)
   static constexpr int KMAX = Dma::KMAX;
+  static constexpr int SPARE = Dma::kSpare ? 1024 : 0;  // target of padding loads
+  static constexpr int LDS = STAGES * BUF + SPARE;
   static constexpr int ISSUE = 2 * KMAX;  // loads each wave issues per stage
 };
 
@@ -405,7 +446,8 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
   typedef Dq16<HD> C;
   typedef typename Frag<T>::type F;
   constexpr int NC = HD / 16, NDB = HD / 32;
-  constexpr int BM = C::BM, BN = C::BN, RB = C::RB;
+  constexpr int BM = C::BM, BN = C::BN;
+  typedef typename C::L L;
 
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
   char* const spare = smem + C::STAGES * C::BUF;
@@ -457,7 +499,7 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
 
   int a_off[NC];
 #pragma unroll
-  for (int cc = 0; cc < NC; ++cc) a_off[cc] = C::L::off(c32, 2 * cc + hl);
+  for (int cc = 0; cc < NC; ++cc) a_off[cc] = L::off(c32, 2 * cc + hl);
   const int gi16 = lane & 15, dh = (lane >> 4) & 1;
   int t_off[NDB][2];
 #pragma unroll
@@ -466,7 +508,7 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
     for (int sec = 0; sec < 2; ++sec) {
       const int r = 4 * hl + 8 * sec + (gi16 >> 2);
       const int col = 32 * db + 16 * dh + 4 * (gi16 & 3);
-      t_off[db][sec] = C::L::off(r, col >> 3) + 2 * (col & 7);
+      t_off[db][sec] = L::off(r, col >> 3) + 2 * (col & 7);
     }
 
   const int n_kt = (Sk + BN - 1) / BN;
@@ -481,8 +523,8 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
   const rsrc_t rv = make_rsrc(Vg, (unsigned)((size_t)Sk * HD * sizeof(T)));
   constexpr unsigned TILEB = BN * HD * sizeof(T);  // source bytes of one key tile
   auto issue_part = [&](int j, char* buf, int k) {
-    kvdma.issue(k, buf, rk, (unsigned)j * TILEB, spare);
-    kvdma.issue(k, buf + C::TILE, rv, (unsigned)j * TILEB, spare);
+    kvdma.issue(k, buf, rk, (unsigned)j * TILEB, spare, lane);
+    kvdma.issue(k, buf + C::TILE, rv, (unsigned)j * TILEB, spare, lane);
   };
   auto issue = [&](int j, char* buf) {
 #pragma unroll
@@ -548,7 +590,7 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const F bk_n = db + 1 < NDB ? lds_frag_tr<T>(cur, t_off[db + 1][0], t_off[db + 1][1])
-                                    : lds_frag_tr<T>(cur, t_off[0][0] + 16 * RB, t_off[0][1] + 16 * RB);
+                                    : lds_frag_tr<T>(cur, t_off[0][0] + L::rows(16), t_off[0][1] + L::rows(16));
         constexpr int per_db = 16 / NDB;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
@@ -565,7 +607,7 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         F bk_n;
-        if (db + 1 < NDB) bk_n = lds_frag_tr<T>(cur, t_off[db + 1][0] + 16 * RB, t_off[db + 1][1] + 16 * RB);
+        if (db + 1 < NDB) bk_n = lds_frag_tr<T>(cur, t_off[db + 1][0] + L::rows(16), t_off[db + 1][1] + L::rows(16));
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) mma_a(dq[mb][db], da[mb][1], bk);
         if (db + 1 < NDB) bk = bk_n;

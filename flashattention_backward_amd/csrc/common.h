@@ -59,6 +59,31 @@ __device__ __forceinline__ void mma_a(f32x16& acc, const bf16x8& a, const bf16x8
 __device__ __forceinline__ void mma_a(f32x16& acc, const f16x8& a, const f16x8& b) {
   asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+// The same with the accumulator in VGPRs, as volatile asm: the statements keep their order
+// relative to each other and to order_point(), which lets a loop state exactly where vector
+// work goes between MFMAs.  mma_v0 starts a contraction (accumulator input 0); its output
+// may not share registers with the operands (early clobber).  Reads of the result by the
+// vector ALU must follow mma_vdrain().
+__device__ __forceinline__ void mma_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mma_v(f32x16& acc, const f16x8& a, const f16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mma_v0(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mma_v0(f32x16& acc, const f16x8& a, const f16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+// Wait states between an mma_v result and vector-ALU reads of it (19 cover the longest
+// MFMA-write to VALU-read distance of a 32x32 MFMA).
+__device__ __forceinline__ void mma_vdrain(f32x16 (&a)[2]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(a[0]), "+v"(a[1]));
+}
+// Marks a point in the volatile-asm order by which x must have been computed.
+__device__ __forceinline__ void order_point(float& x) { asm volatile("" : "+v"(x)); }
+
 // Wait states between the last accumulating MFMA and any other access to its registers
 // (more than the 8 passes plus the read latency of a 32x32x16 MFMA).  Every accumulator is an
 // operand, so no accumulating MFMA can be scheduled after the wait and no read before it.
@@ -136,32 +161,56 @@ __device__ __forceinline__ int perm16(int m) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------------------
-// 16-bit tiles in LDS.  Both access shapes the kernels use must be free of bank conflicts on
-// gfx950: a b128 read of one 16-byte chunk from 32 consecutive rows (operands that contract
-// over the head dim) and a ds_read_b64_tr_b16 of a 4-row x 16-column block per 16-lane group
-// (operands that contract over rows).  Measured layouts that satisfy both:
-//   HD = 128: rows padded to 304 bytes (16 data chunks + 3 pad chunks), chunk c at 16 c;
-//   HD = 64:  unpadded 128-byte rows, chunk c stored at position c ^ swz64(r).
-// Padding keeps every per-lane offset affine in the chunk index, so unrolled loops address
-// the tile with one base register and immediate offsets.
+// 16-bit tiles in LDS.  Two access shapes must be free of bank conflicts on gfx950 (64 banks
+// of 4 bytes, 256 bytes per cycle):
+//   * a b128 read of one 16-byte chunk from 16 consecutive rows (operands that contract over
+//     the head dim: 16 lanes, 256 bytes);
+//   * a ds_read_b64_tr_b16 half-wave, which reads 4 consecutive rows x 64 bytes (4 chunks
+//     starting at a multiple of 4) for operands that contract over rows.
+// HD = 128: rows in groups of four; row b of a group starts 320 bytes (80 dwords, 16 banks
+// mod 64) after row b - 1, groups are 1232 bytes (308 dwords, 4 mod 16) apart.  The four
+// rows of a transposed read then cover disjoint 16-bank windows, and 16 consecutive rows
+// start at 16 distinct multiples of 4 banks.  Every offset stays affine (row data are
+// contiguous, whole groups shift by a constant), so unrolled loops use immediate offsets.
+// HD = 64: unpadded 128-byte rows (two per bank cycle), chunk c of row r at position
+// c ^ swz64(r); the row parity selects the half of the bank cycle.
 __device__ __forceinline__ int swz64(int r) { return 4 * ((r >> 1) & 1) + ((r >> 2) & 3); }
 
 template <int HD>
-struct TileLayout {
-  static constexpr bool kPadded = HD == 128;
-  static constexpr int RB = kPadded ? 304 : 2 * HD;  // bytes per row
-  static constexpr int GPR = RB / 16;                // 16-byte granules per row, padding included
-  static constexpr int CPR = 2 * HD / 16;            // data chunks per row
+struct TileLayout;
+
+template <>
+struct TileLayout<128> {
+  static constexpr int ROWB = 256;                 // data bytes per row
+  static constexpr int SLOT = 320, GROUP = 1232;   // row stride in a group, group stride
+  static constexpr int GPG = GROUP / 16;           // 16-byte granules per group (77)
+  // Bytes of a tile of `rows` rows; byte shift of `n` rows (both multiples of 4).
+  static constexpr int bytes(int rows) { return rows / 4 * GROUP; }
+  static constexpr int rows(int n) { return n / 4 * GROUP; }
   // Byte offset of 16-byte chunk c of row r.
   __device__ static __forceinline__ int off(int r, int c) {
-    if constexpr (kPadded) return r * RB + 16 * c;
-    else return r * RB + 16 * (c ^ swz64(r));
+    return (r >> 2) * GROUP + (r & 3) * SLOT + 16 * c;
   }
-  // Which data chunk of row r granule position pc holds (padding granules repeat chunks
-  // 0..2 of the row, so that every granule of a tile row can be loaded from valid memory).
-  __device__ static __forceinline__ int chunk_at(int r, int pc) {
-    if constexpr (kPadded) return pc < CPR ? pc : pc - CPR;
-    else return pc ^ swz64(r);
+  // Row and chunk whose data the granule at byte 16 gi holds; the gap granules after a row
+  // (4 of them, 1 after the last row of a group) repeat chunks of that row.
+  __device__ static __forceinline__ void granule(int gi, int& r, int& c) {
+    const int g = gi / GPG, q = gi - g * GPG;
+    const int b = min(q / (SLOT / 16), 3);
+    c = q - b * (SLOT / 16);
+    if (c >= 16) c -= 16;
+    r = 4 * g + b;
+  }
+};
+
+template <>
+struct TileLayout<64> {
+  static constexpr int ROWB = 128;
+  static constexpr int bytes(int rows) { return rows * ROWB; }
+  static constexpr int rows(int n) { return n * ROWB; }  // n a multiple of 16
+  __device__ static __forceinline__ int off(int r, int c) { return r * ROWB + 16 * (c ^ swz64(r)); }
+  __device__ static __forceinline__ void granule(int gi, int& r, int& c) {
+    r = gi >> 3;
+    c = (gi & 7) ^ swz64(r);
   }
 };
 
@@ -209,13 +258,13 @@ __device__ __forceinline__ void b2lds16(rsrc_t r, unsigned voff, unsigned soff, 
 // Copy rows [row0, row0 + ROWS) of a row-major [*, HD] tensor slice (rows 0 .. last_row,
 // starting at `src`) into an LDS tile in TileLayout<HD>, with direct loads spread over `nw`
 // waves (this one is wave w).  Rows past `last_row` are loaded from `last_row` (finite data;
-// callers mask them).
+// callers mask them).  Lanes past the tile's last granule do not load.
 template <class T, int HD, int ROWS>
 __device__ __forceinline__ void load_tile(char* tile, const T* src, int row0, int last_row,
                                           int w, int nw, int lane) {
   typedef TileLayout<HD> L;
-  constexpr int NG = ROWS * L::GPR;      // granules in the tile
-  constexpr int NI = (NG + 63) / 64;     // wave instructions (1 KB each)
+  constexpr int NG = L::bytes(ROWS) / 16;  // granules in the tile
+  constexpr int NI = (NG + 63) / 64;       // wave instructions (1 KB each)
   const rsrc_t r = make_rsrc(src, (unsigned)(last_row + 1) * HD * sizeof(T));
 #pragma unroll
   for (int k = 0; k < (NI + 3) / 4; ++k) {
@@ -223,9 +272,10 @@ __device__ __forceinline__ void load_tile(char* tile, const T* src, int row0, in
     if (q < NI) {
       const int gi = 64 * q + lane;
       if (NG % 64 == 0 || gi < NG) {
-        const int rr = gi / L::GPR, pc = gi % L::GPR;
+        int rr, c;
+        L::granule(gi, rr, c);
         const int row = min(row0 + rr, last_row);
-        b2lds16(r, (unsigned)((row * HD + 8 * L::chunk_at(rr, pc)) * sizeof(T)), 0u, tile + 1024 * q);
+        b2lds16(r, (unsigned)((row * HD + 8 * c) * sizeof(T)), 0u, tile + 1024 * q);
       }
     }
   }
@@ -237,32 +287,39 @@ __device__ __forceinline__ void load_tile(char* tile, const T* src, int row0, in
 // (soffset), so each instruction needs no per-lane address arithmetic.  Rows past the end
 // of the resource read as zeros.  Every wave issues KMAX instructions: where the tile has no
 // instruction left for a wave, it writes to `spare` (1 KB of LDS nothing reads), which keeps
-// the per-wave load count uniform for the vmcnt waits and the issue free of branches.  The
-// last instruction of a tile may cover fewer granules than lanes; the extra lanes write into
-// the tile's rounding slack (tiles are rounded up to whole KB).
+// the per-wave load count uniform for the vmcnt waits.  The tile's last instruction may
+// cover fewer granules than lanes; only its valid lanes load.
 template <class T, int HD, int ROWS>
 struct TileDma {
   typedef TileLayout<HD> L;
-  static constexpr int NG = ROWS * L::GPR;
+  static constexpr int NG = L::bytes(ROWS) / 16;
   static constexpr int NI = (NG + 63) / 64;   // wave instructions for the whole tile
   static constexpr int KMAX = (NI + 3) / 4;   // instructions each of 4 waves issues
-  static constexpr unsigned ROWB = HD * sizeof(T);  // bytes per source row
-  static_assert(NG % 64 == 0 || (NG % 64) * 16 + (NI - 1) * 1024 <= NI * 1024, "slack");
+  static constexpr bool kSpare = 4 * KMAX > NI;
+  static constexpr int TAIL = NG % 64;        // valid lanes of the last instruction (0: all)
   int w;
   unsigned src_off[KMAX];  // byte offset of this lane's granule of instruction k from row 0
   __device__ __forceinline__ void init(int wave, int lane) {
     w = wave;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
-      const int gi = 64 * (w + 4 * k) + lane;
-      const int r = gi / L::GPR, pc = gi % L::GPR;
-      src_off[k] = (unsigned)r * ROWB + (unsigned)(8 * L::chunk_at(r, pc) * sizeof(T));
+      int r, c;
+      L::granule(64 * (w + 4 * k) + lane, r, c);
+      src_off[k] = (unsigned)((r * HD + 8 * c) * sizeof(T));
     }
   }
   // Instruction k of this wave: the tile whose first row starts at byte `soff` of `r`.
-  __device__ __forceinline__ void issue(int k, char* tile, rsrc_t r, unsigned soff, char* spare) const {
-    char* dst = (w + 4 * k < NI) ? tile + 1024 * (w + 4 * k) : spare;
-    b2lds16(r, src_off[k], soff, dst);
+  __device__ __forceinline__ void issue(int k, char* tile, rsrc_t r, unsigned soff, char* spare,
+                                        int lane) const {
+    const int q = w + 4 * k;
+    if (kSpare && 4 * k + 3 >= NI) {  // instruction k does not exist for every wave
+      char* dst = q < NI ? tile + 1024 * q : spare;
+      if (TAIL == 0 || q != NI - 1 || lane < TAIL) b2lds16(r, src_off[k], soff, dst);
+    } else if (TAIL != 0 && 4 * k + 3 >= NI - 1) {
+      if (q != NI - 1 || lane < TAIL) b2lds16(r, src_off[k], soff, tile + 1024 * q);
+    } else {
+      b2lds16(r, src_off[k], soff, tile + 1024 * q);
+    }
   }
 };
 
@@ -272,10 +329,14 @@ __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)
 // global memory operation of the wave (vmcnt(0)), which would stall on the tiles being
 // prefetched; here each wave first drains only its LDS reads (so no wave can still be reading
 // a buffer that the next step's prefetch overwrites) and the caller waits explicitly for the
-// tile the next step needs (wait_vm_le).  The empty asm blocks with a memory clobber stop
-// the compiler from moving LDS accesses across the barrier.
+// tile the next step needs (wait_vm_le).  The asm blocks with a memory clobber stop the
+// compiler from moving LDS accesses across the barrier; the LDS wait is issued through the
+// builtin so that the compiler's own wait-count tracking knows every earlier LDS read has
+// completed (it does not look inside asm text).
 __device__ __forceinline__ void barrier_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at "no wait"
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding (loads return
