@@ -34,13 +34,36 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 EXTRA_FLAGS = {"bwd16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
+# Sources with inline-asm MFMAs: compiled with -save-temps so that the device assembly of the
+# very object that is linked can be checked for operand hazards (asm_check).
+ASM_CHECKED = {"bwd16.hip"}
+
+
+def device_asm_path(src: str) -> str:
+    stem = os.path.splitext(src)[0]
+    return os.path.join(BUILD, stem + "_temps", f"{stem}-hip-amdgcn-amd-amdhsa-gfx950.s")
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *DEVICE_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", os.path.join(ROOT, "include"),
            "-c", os.path.join(CSRC, src), "-o", obj]
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    cwd = None
+    if src in ASM_CHECKED:
+        cwd = os.path.dirname(device_asm_path(src))
+        os.makedirs(cwd, exist_ok=True)
+        cmd.append("-save-temps")
+    r = subprocess.run(cmd, capture_output=True, text=True, cwd=cwd)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    if src in ASM_CHECKED:
+        from . import asm_check
+        with open(device_asm_path(src)) as fh:
+            asm = fh.read()
+        bad = asm_check.mfma_operand_hazards(asm)
+        if bad:
+            lines = "\n".join(f"  {p}  ->  {m}" for p, m in bad[:10])
+            raise RuntimeError(f"{src}: {len(bad)} MFMA operand hazard(s) in the compiled code:\n{lines}")
     return obj
 
 

@@ -308,7 +308,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
       bq[db] = b_q(db, 0);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        mma_a(dv[nb][db], pa[nb][0], bo[db]);
+        if (db == 0) mma_a<true>(dv[nb][db], pa[nb][0], bo[db]);  // first use of pa[nb][0]
+        else mma_a(dv[nb][db], pa[nb][0], bo[db]);
 #pragma unroll
         for (int k = 0; k < PER_MMA; ++k) {
           const int e = (2 * db + nb) * PER_MMA + k;  // 0..15 over rows 0..15 of both blocks
@@ -323,7 +324,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
       bo[db] = b_do(db, 1);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        mma_a(dk[nb][db], da[nb][0], bq[db]);
+        if (db == 0) mma_a<true>(dk[nb][db], da[nb][0], bq[db]);  // first use of da[nb][0]
+        else mma_a(dk[nb][db], da[nb][0], bq[db]);
 #pragma unroll
         for (int k = 0; k < PER_MMA; ++k) {
           const int e = (2 * db + nb) * PER_MMA + k;
@@ -337,7 +339,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
     for (int db = 0; db < NDB; ++db) {
       bq[db] = b_q(db, 1);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) mma_a(dv[nb][db], pa[nb][1], bo[db]);
+      for (int nb = 0; nb < 2; ++nb) {
+        if (db == 0) mma_a<true>(dv[nb][db], pa[nb][1], bo[db]);
+        else mma_a(dv[nb][db], pa[nb][1], bo[db]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     // ---- end of the step for the workgroup: the next stage has landed (the loads of the one
@@ -349,7 +354,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) mma_a(dk[nb][db], da[nb][1], bq[db]);
+      for (int nb = 0; nb < 2; ++nb) {
+        if (db == 0) mma_a<true>(dk[nb][db], da[nb][1], bq[db]);
+        else mma_a(dk[nb][db], da[nb][1], bq[db]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };

@@ -49,41 +49,24 @@ __device__ __forceinline__ void mma(f32x16& acc, const f32x8& a, const f32x8& b)
 // acc += A * B with the accumulator pinned to AGPRs (the "a" constraint).  Used for the
 // long-lived accumulators (dK, dV, dQ) so that the register allocator never moves them
 // between the AGPR and VGPR files; the short-lived score tiles use mma() in VGPRs.
-// Hazards handled here, because the compiler does not look inside the asm: `s_nop 1` gives
-// the two wait states needed between a VALU write of an A/B operand and the MFMA reading it;
-// consecutive MFMAs accumulating into the same registers need none; reads of the
+// Hazards are handled by the caller, because the compiler does not look inside the asm: a
+// VALU write of an A/B operand needs two wait states before the MFMA reads it.  NOP = true
+// (the default) puts them in front (`s_nop 1`).  Dropping them where no producer can be
+// that close was measured slower on gfx950 (the compiler schedules the shorter asm
+// differently), so every asm MFMA keeps them; the build checks the compiled code for this
+// hazard either way (asm_check.py).  Consecutive
+// MFMAs accumulating into the same registers need no wait states; reads of the
 // accumulators after the last MFMA must go through mma_drain() first.
+template <bool NOP = true>
 __device__ __forceinline__ void mma_a(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  if constexpr (NOP) asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+template <bool NOP = true>
 __device__ __forceinline__ void mma_a(f32x16& acc, const f16x8& a, const f16x8& b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  if constexpr (NOP) asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
-// The same with the accumulator in VGPRs, as volatile asm: the statements keep their order
-// relative to each other and to order_point(), which lets a loop state exactly where vector
-// work goes between MFMAs.  mma_v0 starts a contraction (accumulator input 0); its output
-// may not share registers with the operands (early clobber).  Reads of the result by the
-// vector ALU must follow mma_vdrain().
-__device__ __forceinline__ void mma_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mma_v(f32x16& acc, const f16x8& a, const f16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mma_v0(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mma_v0(f32x16& acc, const f16x8& a, const f16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
-}
-// Wait states between an mma_v result and vector-ALU reads of it (19 cover the longest
-// MFMA-write to VALU-read distance of a 32x32 MFMA).
-__device__ __forceinline__ void mma_vdrain(f32x16 (&a)[2]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(a[0]), "+v"(a[1]));
-}
-// Marks a point in the volatile-asm order by which x must have been computed.
-__device__ __forceinline__ void order_point(float& x) { asm volatile("" : "+v"(x)); }
-
 // Wait states between the last accumulating MFMA and any other access to its registers
 // (more than the 8 passes plus the read latency of a 32x32x16 MFMA).  Every accumulator is an
 // operand, so no accumulating MFMA can be scheduled after the wait and no read before it.
@@ -93,6 +76,38 @@ __device__ __forceinline__ void mma_drain(f32x16 (&a)[4]) {
 __device__ __forceinline__ void mma_drain(f32x16 (&a)[2]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(a[0]), "+a"(a[1]));
 }
+// The same with the accumulator in VGPRs, as volatile asm: the statements keep their order
+// relative to each other and to order_point(), which lets a loop state exactly where vector
+// work goes between MFMAs.  mma_v0 starts a contraction (accumulator input 0); its output
+// may not share registers with the operands (early clobber).  Reads of the result by the
+// vector ALU must follow mma_vdrain().  NOP as for mma_a.
+template <bool NOP = true>
+__device__ __forceinline__ void mma_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  if constexpr (NOP) asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+template <bool NOP = true>
+__device__ __forceinline__ void mma_v(f32x16& acc, const f16x8& a, const f16x8& b) {
+  if constexpr (NOP) asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  else asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+template <bool NOP = true>
+__device__ __forceinline__ void mma_v0(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  if constexpr (NOP) asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+template <bool NOP = true>
+__device__ __forceinline__ void mma_v0(f32x16& acc, const f16x8& a, const f16x8& b) {
+  if constexpr (NOP) asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  else asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+// Wait states between an mma_v result and vector-ALU reads of it (19 cover the longest
+// MFMA-write to VALU-read distance of a 32x32 MFMA).
+__device__ __forceinline__ void mma_vdrain(f32x16 (&a)[2]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(a[0]), "+v"(a[1]));
+}
+// Marks a point in the volatile-asm order by which x must have been computed.
+__device__ __forceinline__ void order_point(float& x) { asm volatile("" : "+v"(x)); }
 
 // 8 consecutive elements <-> fragment.  16-bit types move as one 16-byte access, fp32 as
 // two, so only 16-byte alignment is ever required.
