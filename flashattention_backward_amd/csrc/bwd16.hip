@@ -429,16 +429,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
 }
 
 // =======================================================================================
-// dQ: query-tile outer.  A workgroup owns BM = 256 query rows of one (batch, head); wave w
-// owns rows [64 w, 64 w + 64) (two 32-row blocks) with their Q and dO fragments, LSE and D in
-// registers.  Per step of BN = 32 keys it recomputes S^T = K Q^T and dP^T = V dO^T (one query
-// row per lane), forms dS^T = P^T (dP^T - D) and adds dS K into the dQ accumulators.  K and V
-// tiles stream through a double-buffered LDS stage.
+// dQ: query-tile outer.  A workgroup owns BM = 128 MB query rows of one (batch, head); wave w
+// owns MB 32-row blocks with their Q and dO fragments, LSE and D in registers.  Per step of
+// BN = 32 keys it recomputes S^T = K Q^T and dP^T = V dO^T (one query row per lane), forms
+// dS^T = P^T (dP^T - D) and adds dS K into the dQ accumulators.  K and V tiles stream through
+// a three-stage LDS ring.
 // =======================================================================================
-template <int HD>
+template <int HD, int MB>
 struct Dq16 {
   typedef TileLayout<HD> L;
-  static constexpr int BM = 256, BN = 32;
+  static constexpr int BM = 4 * 32 * MB, BN = 32;  // MB 32-row blocks per wave
   static constexpr int TILE = L::bytes(BN);  // one K or V tile
   static constexpr int BUF = 2 * TILE;
   static constexpr int STAGES = 3;
@@ -449,9 +449,9 @@ struct Dq16 {
   static constexpr int ISSUE = 2 * KMAX;  // loads each wave issues per stage
 };
 
-template <class T, int HD>
-__global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
-  typedef Dq16<HD> C;
+template <class T, int HD, int MB>
+__global__ __launch_bounds__(256, MB == 1 ? 2 : 1) void bwd_dq16_kernel(const BwdParams p) {
+  typedef Dq16<HD, MB> C;
   typedef typename Frag<T>::type F;
   constexpr int NC = HD / 16, NDB = HD / 32;
   constexpr int BM = C::BM, BN = C::BN;
@@ -474,7 +474,7 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
   const int tq = wi.step / G;
   const int it = causal ? n_qt - 1 - tq : tq;
   const int m0 = it * BM;
-  const int mw0 = m0 + 64 * w;
+  const int mw0 = m0 + 32 * MB * w;
 
   const size_t q_off = (size_t)(b * p.H + hq) * Sq;
   const size_t kv_off = (size_t)(b * p.H_kv + g) * Sk * HD;
@@ -483,10 +483,10 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
   const T* Kg = (const T*)p.k + kv_off;
   const T* Vg = (const T*)p.v + kv_off;
 
-  F qf[2][NC], dof[2][NC];
-  float lse2[2], dl[2];
+  F qf[MB][NC], dof[MB][NC];
+  float lse2[MB], dl[MB];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int mb = 0; mb < MB; ++mb) {
     const int m = mw0 + 32 * mb + c32;
     const int mc = min(m, Sq - 1);
 #pragma unroll
@@ -499,9 +499,9 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
     dl[mb] = m < Sq ? st[1] : 0.f;
   }
 
-  f32x16 dq[2][NDB];
+  f32x16 dq[MB][NDB];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dq[mb][db] = f32x16{};
 
@@ -549,9 +549,9 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
   auto step_body = [&](const char* __restrict__ cur, char* __restrict__ nxt, int j) {
     const int n0 = j * BN;
     {
-      f32x16 St[2], dPt[2];
+      f32x16 St[MB], dPt[MB];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < MB; ++mb) {
         St[mb] = f32x16{};
         dPt[mb] = f32x16{};
       }
@@ -561,21 +561,21 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
         const F av = lds_frag<T>(cur + C::TILE, a_off[cc]);
         if (cc < C::KMAX) issue_part(j + 2, nxt, cc);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
           mma(St[mb], ak, qf[mb][cc]);
           mma(dPt[mb], av, dof[mb][cc]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      F da[2][2];
+      F da[MB][2];
       // Masking, only on steps that need it (the causal diagonal, the last key tile): a cut
       // score is replaced by mask_s, whose exponent is -inf.  Register r of this lane holds
       // key n0 + 4 hl + off(r), off = 8 (r / 4) + r % 4, of row m (one row per lane); it may be
       // seen iff off < min(Sk, causal ? m + 1 : Sk) - n0 - 4 hl.
       if ((n0 + BN > Sk) || (causal && n0 + BN - 1 > mw0)) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
           const int m = mw0 + 32 * mb + c32;
           const int lim = (causal ? min(Sk, m + 1) : Sk) - n0 - 4 * hl;
 #pragma unroll
@@ -590,7 +590,7 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
         da[mb][r >> 3][r & 7] = (T)(pv * (dPt[mb][r] - dl[mb]));
       };
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 8; ++r) elem(mb, r);
       // dQ += dS K for key slice 0 with the softmax of slice 1 woven in, then slice 1.
@@ -599,13 +599,13 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
       for (int db = 0; db < NDB; ++db) {
         const F bk_n = db + 1 < NDB ? lds_frag_tr<T>(cur, t_off[db + 1][0], t_off[db + 1][1])
                                     : lds_frag_tr<T>(cur, t_off[0][0] + L::rows(16), t_off[0][1] + L::rows(16));
-        constexpr int per_db = 16 / NDB;
+        constexpr int PER = 8 / NDB;  // slice-1 elements per MFMA
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
           mma_a(dq[mb][db], da[mb][0], bk);
 #pragma unroll
-          for (int k = 0; k < per_db / 2; ++k) {
-            const int e = db * per_db + mb * (per_db / 2) + k;  // 0..15 over slice 1
+          for (int k = 0; k < PER; ++k) {
+            const int e = (db * MB + mb) * PER + k;  // 0 .. 8 MB - 1 over slice 1
             elem(e >> 3, 8 + (e & 7));
           }
         }
@@ -617,7 +617,7 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
         F bk_n;
         if (db + 1 < NDB) bk_n = lds_frag_tr<T>(cur, t_off[db + 1][0] + L::rows(16), t_off[db + 1][1] + L::rows(16));
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) mma_a(dq[mb][db], da[mb][1], bk);
+        for (int mb = 0; mb < MB; ++mb) mma_a(dq[mb][db], da[mb][1], bk);
         if (db + 1 < NDB) bk = bk_n;
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -634,11 +634,11 @@ __global__ __launch_bounds__(256) void bwd_dq16_kernel(const BwdParams p) {
   }
   wait_vm_all();  // no prefetch may still be writing LDS when the workgroup ends
 
-  mma_drain(dq[0]);
-  mma_drain(dq[1]);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) mma_drain(dq[mb]);
   T* dQg = (T*)p.dq + q_off * HD;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -658,13 +658,22 @@ static hipError_t go_dkdv(const BwdParams& p, hipStream_t s, LaunchInfo* info) {
   return hipGetLastError();
 }
 
+// 32-row blocks per wave of the dQ kernel.  1 (128-row workgroups, two per CU, two waves per
+// SIMD) measured 5 % faster than 2 (256-row workgroups, one wave per SIMD) on the headline
+// shape: the second wave on a SIMD issues while the first waits, which outweighs reading
+// the K and V fragments twice as often from LDS.
+#ifndef FAB_DQ_MB
+#define FAB_DQ_MB 1
+#endif
+constexpr int kDqMB = FAB_DQ_MB;
+
 template <class T, int HD>
 static hipError_t go_dq(const BwdParams& p, hipStream_t s, LaunchInfo* info) {
-  typedef Dq16<HD> C;
+  typedef Dq16<HD, kDqMB> C;
   const int n_qt = (p.Sq + C::BM - 1) / C::BM;
   const int grid = p.n_units * (p.H / p.H_kv) * n_qt;
   if (info) *info = LaunchInfo{"bwd_dq16", grid, 256, C::LDS};
-  hipLaunchKernelGGL((bwd_dq16_kernel<T, HD>), dim3(grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((bwd_dq16_kernel<T, HD, kDqMB>), dim3(grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
