@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfab.so")
-SOURCES = ["api.hip", "preprocess.hip", "bwd_dkdv.hip", "bwd_dq.hip", "bwd16.hip", "fwd.hip"]
+SOURCES = ["api.hip", "preprocess.hip", "bwd_dkdv.hip", "bwd_dq.hip", "bwd16.hip", "fwd.hip", "fwd16.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 # Packed-fp32 VALU forms are disabled for all device code (see the design notes).
@@ -31,7 +31,8 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 # Per-source extra flags.  bwd16.hip keeps its long-lived accumulators in AGPRs through
 # inline-asm MFMAs; every other MFMA there is selected in VGPR form so that the short-lived
 # score tiles never compete with the accumulators for AGPRs.
-EXTRA_FLAGS = {"bwd16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA_FLAGS = {"bwd16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "fwd16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 # Sources with inline-asm MFMAs: compiled with -save-temps so that the device assembly of the

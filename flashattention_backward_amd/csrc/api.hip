@@ -242,7 +242,9 @@ fab_status fab_fwd(const void* q, const void* k, const void* v, void* o, float* 
   p.n_units = B * H_kv;
   p.units_per_xcd = units_per_xcd(p.n_units);
   fab::LaunchInfo li;
-  FAB_TRY(launched(fab::launch_fwd(p, dtype, D, (hipStream_t)stream, &li), "fwd"));
+  const hipError_t e = dtype == FAB_F32 ? fab::launch_fwd(p, dtype, D, (hipStream_t)stream, &li)
+                                        : fab::launch_fwd16(p, dtype, D, (hipStream_t)stream, &li);
+  FAB_TRY(launched(e, "fwd"));
   log_launch(li);
   return FAB_OK;
 }
