@@ -5,7 +5,8 @@ One step = one complete backward call (fab_bwd: preprocess D = rowsum(dO*O), the
 outer dK/dV kernel and the query-tile outer dQ kernel) over the headline workload -- bf16,
 grouped-query (32 query heads on 8 kv heads), causal, B=2, S=4096, D=128 -- with every input
 (Q, K, V, dO and the forward's O and LSE) already resident in HBM.  The forward that produces
-O and LSE runs once before timing and is not part of a step.
+O and LSE is not part of a step; it is timed on its own afterwards and reported beside the
+metric (`forward`, counting 4*B*H*Sq*Sk*D FLOPs, halved when causal).
 
 Metric: attention-backward TFLOP/s counting 10*B*H*Sq*Sk*D FLOPs per step, halved when causal
 (the five contractions over the pairs the method must visit), and its fraction of MI355X's
@@ -17,7 +18,7 @@ on the launch stream) and a `cpu_baseline` object (the fp64 oracle's backward on
 sample of the same workload, timed on this host's cores before the GPU is touched).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
-       python bench.py --only {bwd,dkdv,dq,preprocess,copy}   (a launch loop for rocprofv3)
+       python bench.py --only {bwd,dkdv,dq,preprocess,fwd,copy}   (a launch loop for rocprofv3)
 """
 from __future__ import annotations
 
@@ -53,10 +54,15 @@ def allowed_pairs(w) -> float:
 
 
 def source_digest(kernel: str) -> str:
+    """sha256 (first 16 hex digits) of the kernel's sources with // comments and blank space
+    removed, so that only a change to the code itself invalidates recorded counters."""
     h = hashlib.sha256()
     for f in (KERNEL_SOURCE[kernel], "common.h", "launch.h"):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].strip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
@@ -157,6 +163,13 @@ class Bwd:
                                 self.dq.data_ptr(), self.dk.data_ptr(), self.dv.data_ptr(),
                                 self.ws.data_ptr(), self.ws.numel(), *self.dims, self.stream))
 
+    def fwd(self):
+        """The supporting forward into the preallocated O and LSE (not part of the metric)."""
+        w = self.w
+        self._ok(self.L.fab_fwd(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),
+                                self.o.data_ptr(), self.lse.data_ptr(), w.B, w.H, w.H_kv, w.Sq, w.Sk,
+                                w.D, self.code, int(w.causal), float(w.scale), self.stream))
+
     def preprocess(self):
         w = self.w
         self._ok(self.L.fab_bwd_preprocess(self.do.data_ptr(), self.o.data_ptr(), self.lse.data_ptr(),
@@ -228,6 +241,10 @@ def bench_workload(w, steps, warmup, with_cpu, inputs=None):
     k_ms = {"preprocess": time_launches(b.preprocess, steps, warmup),
             "bwd_dkdv": time_launches(b.dkdv, steps, warmup),
             "bwd_dq": time_launches(b.dq_, steps, warmup)}
+    # the supporting forward, reported beside the metric (4 of the 10 counted units per pair);
+    # it rewrites the same O and LSE, so the backward's inputs do not change
+    fwd_ms = time_launches(b.fwd, steps, warmup)
+    fwd_tflops = 0.4 * w.bwd_flops() / (fwd_ms * 1e-3) / 1e12
     flops = w.bwd_flops()
     tflops = flops / (ms * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[w.dtype]
@@ -256,6 +273,8 @@ def bench_workload(w, steps, warmup, with_cpu, inputs=None):
         "wall_ms_per_step": round(wall_ms, 4),
         "kernel_ms": {n: round(t, 4) for n, t in k_ms.items()},
         "preprocess_GBps": round(pre_bytes / (k_ms["preprocess"] * 1e-3) / 1e9, 1),
+        "forward": {"ms": round(fwd_ms, 4), "tflops": round(fwd_tflops, 2),
+                    "frac_of_peak": round(fwd_tflops / peak, 4)},
         "roofline": {
             "kernel": dom,
             "bound": "mfma",
@@ -286,7 +305,7 @@ def only_mode(w, what, steps, warmup):
                           "launches": warmup + steps}), flush=True)
         return
     b = Bwd(w, *workloads.make_inputs(w))
-    fn = {"bwd": b.bwd, "dkdv": b.dkdv, "dq": b.dq_, "preprocess": b.preprocess}[what]
+    fn = {"bwd": b.bwd, "dkdv": b.dkdv, "dq": b.dq_, "preprocess": b.preprocess, "fwd": b.fwd}[what]
     if what in ("dkdv", "dq"):
         b.preprocess()
     for _ in range(warmup + steps):
@@ -303,7 +322,7 @@ def main():
     ap.add_argument("--workload", default=workloads.HEADLINE, choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--all", action="store_true", help="one JSON line per named workload (no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["bwd", "dkdv", "dq", "preprocess", "copy"])
+    ap.add_argument("--only", choices=["bwd", "dkdv", "dq", "preprocess", "fwd", "copy"])
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

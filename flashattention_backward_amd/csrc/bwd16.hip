@@ -2,11 +2,13 @@
 //
 // Both kernels stage their streamed operand tiles with direct global->LDS loads
 // (buffer_load_dwordx4 ... lds) into a ring of stage buffers, so the next tiles arrive while
-// the current one is consumed and each step needs one barrier.  Tiles are row-major and XOR-swizzled
-// (swz in common.h); operands that contract over rows are read with the LDS transpose read
-// (lds_frag_tr) instead of keeping a transposed copy.  Rows past the end of a sequence are
-// loaded from the last valid row (finite data) and neutralised by the masks and by the
-// per-row statistics the preprocess writes for padding rows (LSE = +inf, D = 0).
+// the current one is consumed and each step needs one barrier.  Tiles are row-major in the
+// bank-conflict-free layouts of TileLayout (common.h); operands that contract over rows are
+// read with the LDS transpose read (lds_frag_tr) instead of keeping a transposed copy.  The
+// buffer loads are range-checked: rows past the end of the tensor read as zeros and rows
+// past a head's end read the next head's rows, finite values that the masks and the padding
+// rows' statistics (LSE = +inf, D = 0) neutralise.  (The dK/dV kernel's resident V tile is
+// loaded once with plain loads clamped to the last valid key.)
 //
 // Per-row statistics: stats[(b*H + h) * Sq_pad + i] = {LSE * log2(e), D} with
 // Sq_pad = Sq rounded up to 64 (written by the preprocess kernel).
@@ -435,26 +437,27 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
 // dS^T = P^T (dP^T - D) and adds dS K into the dQ accumulators.  K and V tiles stream through
 // a three-stage LDS ring.
 // =======================================================================================
-template <int HD, int MB>
+template <int HD, int NB>
 struct Dq16 {
   typedef TileLayout<HD> L;
-  static constexpr int BM = 4 * 32 * MB, BN = 32;  // MB 32-row blocks per wave
-  static constexpr int TILE = L::bytes(BN);  // one K or V tile
+  static constexpr int BM = 128, BN = 32 * NB;  // one 32-row block per wave, NB key blocks
+  static constexpr int TILE = L::bytes(BN);     // one K or V tile
   static constexpr int BUF = 2 * TILE;
-  static constexpr int STAGES = 3;
+  static constexpr int STAGES = NB == 1 ? 3 : 2;  // two workgroups per CU either way
   typedef TileDma<bf16, HD, BN> Dma;  // (the element type only sets the row size)
   static constexpr int KMAX = Dma::KMAX;
   static constexpr int SPARE = Dma::kSpare ? 1024 : 0;  // target of padding loads
   static constexpr int LDS = STAGES * BUF + SPARE;
   static constexpr int ISSUE = 2 * KMAX;  // loads each wave issues per stage
+  static_assert(LDS <= 80 * 1024, "two workgroups per CU");
 };
 
-template <class T, int HD, int MB>
-__global__ __launch_bounds__(256, MB == 1 ? 2 : 1) void bwd_dq16_kernel(const BwdParams p) {
-  typedef Dq16<HD, MB> C;
+template <class T, int HD, int NB>
+__global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(const BwdParams p) {
+  typedef Dq16<HD, NB> C;
   typedef typename Frag<T>::type F;
   constexpr int NC = HD / 16, NDB = HD / 32;
-  constexpr int BM = C::BM, BN = C::BN;
+  constexpr int BM = C::BM, BN = C::BN, STAGES = C::STAGES;
   typedef typename C::L L;
 
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
@@ -472,9 +475,10 @@ __global__ __launch_bounds__(256, MB == 1 ? 2 : 1) void bwd_dq16_kernel(const Bw
   const int b = wi.unit / p.H_kv, g = wi.unit % p.H_kv;
   const int hq = g * G + wi.step % G;
   const int tq = wi.step / G;
-  const int it = causal ? n_qt - 1 - tq : tq;
+  const int it = causal ? n_qt - 1 - tq : tq;  // heaviest query tiles first
   const int m0 = it * BM;
-  const int mw0 = m0 + 32 * MB * w;
+  const int mw0 = m0 + 32 * w;
+  const int m = mw0 + c32;  // this lane's query row
 
   const size_t q_off = (size_t)(b * p.H + hq) * Sq;
   const size_t kv_off = (size_t)(b * p.H_kv + g) * Sk * HD;
@@ -483,27 +487,23 @@ __global__ __launch_bounds__(256, MB == 1 ? 2 : 1) void bwd_dq16_kernel(const Bw
   const T* Kg = (const T*)p.k + kv_off;
   const T* Vg = (const T*)p.v + kv_off;
 
-  F qf[MB][NC], dof[MB][NC];
-  float lse2[MB], dl[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int m = mw0 + 32 * mb + c32;
+  F qf[NC], dof[NC];
+  float lse2, dl;
+  {
     const int mc = min(m, Sq - 1);
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
-      qf[mb][cc] = ld8(Qg + (size_t)mc * HD + 16 * cc + 8 * hl);
-      dof[mb][cc] = ld8(dOg + (size_t)mc * HD + 16 * cc + 8 * hl);
+      qf[cc] = ld8(Qg + (size_t)mc * HD + 16 * cc + 8 * hl);
+      dof[cc] = ld8(dOg + (size_t)mc * HD + 16 * cc + 8 * hl);
     }
     const float* st = p.stats + ((size_t)(b * p.H + hq) * p.Sq_pad + mc) * 2;
-    lse2[mb] = m < Sq ? st[0] : __builtin_inff();
-    dl[mb] = m < Sq ? st[1] : 0.f;
+    lse2 = m < Sq ? st[0] : __builtin_inff();
+    dl = m < Sq ? st[1] : 0.f;
   }
 
-  f32x16 dq[MB][NDB];
+  f32x16 dq[NDB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) dq[mb][db] = f32x16{};
+  for (int db = 0; db < NDB; ++db) dq[db] = f32x16{};
 
   int a_off[NC];
 #pragma unroll
@@ -534,118 +534,103 @@ __global__ __launch_bounds__(256, MB == 1 ? 2 : 1) void bwd_dq16_kernel(const Bw
     kvdma.issue(k, buf, rk, (unsigned)j * TILEB, spare, lane);
     kvdma.issue(k, buf + C::TILE, rv, (unsigned)j * TILEB, spare, lane);
   };
-  auto issue = [&](int j, char* buf) {
 #pragma unroll
-    for (int k = 0; k < C::KMAX; ++k) issue_part(j, buf, k);
-  };
-
-  issue(0, smem);
-  issue(1, smem + C::BUF);
-  wait_vm_le<C::ISSUE>();  // Q, dO, statistics and stage 0 have landed
+  for (int s = 0; s < STAGES - 1; ++s)
+#pragma unroll
+    for (int k = 0; k < C::KMAX; ++k) issue_part(s, smem + s * C::BUF, k);
+  wait_vm_le<C::ISSUE * (STAGES - 2)>();  // Q, dO, statistics and stage 0 have landed
   barrier_lds();
   const float mask_s = p.mask_s;
 
-  // One step; restrict pointers as in the dK/dV kernel.
+  // One step of BN keys; restrict pointers as in the dK/dV kernel.  `nxt` receives the tile
+  // STAGES - 1 steps ahead.
   auto step_body = [&](const char* __restrict__ cur, char* __restrict__ nxt, int j) {
     const int n0 = j * BN;
-    {
-      f32x16 St[MB], dPt[MB];
+    f32x16 St[NB], dPt[NB];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        St[mb] = f32x16{};
-        dPt[mb] = f32x16{};
-      }
+    for (int nb = 0; nb < NB; ++nb) {
+      St[nb] = f32x16{};
+      dPt[nb] = f32x16{};
+    }
+    // ---- S^T = K Q^T and dP^T = V dO^T per 32-key block; the prefetch is spread over them.
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) {
-        const F ak = lds_frag<T>(cur, a_off[cc]);
-        const F av = lds_frag<T>(cur + C::TILE, a_off[cc]);
-        if (cc < C::KMAX) issue_part(j + 2, nxt, cc);
+    for (int cc = 0; cc < NC; ++cc) {
+      if (cc < C::KMAX) issue_part(j + STAGES - 1, nxt, cc);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          mma(St[mb], ak, qf[mb][cc]);
-          mma(dPt[mb], av, dof[mb][cc]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int nb = 0; nb < NB; ++nb) {
+        const F ak = lds_frag<T>(cur + L::rows(32 * nb), a_off[cc]);
+        const F av = lds_frag<T>(cur + C::TILE + L::rows(32 * nb), a_off[cc]);
+        mma(St[nb], ak, qf[cc]);
+        mma(dPt[nb], av, dof[cc]);
       }
       __builtin_amdgcn_sched_barrier(0);
-      F da[MB][2];
-      // Masking, only on steps that need it (the causal diagonal, the last key tile): a cut
-      // score is replaced by mask_s, whose exponent is -inf.  Register r of this lane holds
-      // key n0 + 4 hl + off(r), off = 8 (r / 4) + r % 4, of row m (one row per lane); it may be
-      // seen iff off < min(Sk, causal ? m + 1 : Sk) - n0 - 4 hl.
-      if ((n0 + BN > Sk) || (causal && n0 + BN - 1 > mw0)) {
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    F da[NB][2];
+    // Masking, only on steps that need it (the causal diagonal, the last key tile): a cut
+    // score is replaced by mask_s, whose exponent is -inf.  Register r of block nb holds key
+    // n0 + 32 nb + 4 hl + off(r), off = 8 (r / 4) + r % 4, of row m (one row per lane); it may
+    // be seen iff off < min(Sk, causal ? m + 1 : Sk) - n0 - 32 nb - 4 hl.
+    if ((n0 + BN > Sk) || (causal && n0 + BN - 1 > mw0)) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int m = mw0 + 32 * mb + c32;
-          const int lim = (causal ? min(Sk, m + 1) : Sk) - n0 - 4 * hl;
+      for (int nb = 0; nb < NB; ++nb) {
+        const int lim = (causal ? min(Sk, m + 1) : Sk) - n0 - 32 * nb - 4 * hl;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = 8 * (r >> 2) + (r & 3);
-            St[mb][r] = off < lim ? St[mb][r] : mask_s;
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int off = 8 * (r >> 2) + (r & 3);
+          St[nb][r] = off < lim ? St[nb][r] : mask_s;
         }
       }
-      auto elem = [&](int mb, int r) {
-        const float pv = fast_exp2(St[mb][r] * p.scale_log2 - lse2[mb]);
-        da[mb][r >> 3][r & 7] = (T)(pv * (dPt[mb][r] - dl[mb]));
-      };
+    }
+    // dS for register r of block nb.
+    auto elem = [&](int nb, int r) {
+      const float pv = fast_exp2(St[nb][r] * p.scale_log2 - lse2);
+      da[nb][r >> 3][r & 7] = (T)(pv * (dPt[nb][r] - dl));
+    };
+    // ---- dQ += dS K, one 16-key slice (sl = 2 nb + ks) at a time; the dS of the next slice
+    // is formed while the current slice's MFMAs run.
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+    for (int r = 0; r < 8; ++r) elem(0, r);
+    constexpr int PER = 8 / NDB;  // next-slice elements per MFMA
 #pragma unroll
-        for (int r = 0; r < 8; ++r) elem(mb, r);
-      // dQ += dS K for key slice 0 with the softmax of slice 1 woven in, then slice 1.
-      F bk = lds_frag_tr<T>(cur, t_off[0][0], t_off[0][1]);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const F bk_n = db + 1 < NDB ? lds_frag_tr<T>(cur, t_off[db + 1][0], t_off[db + 1][1])
-                                    : lds_frag_tr<T>(cur, t_off[0][0] + L::rows(16), t_off[0][1] + L::rows(16));
-        constexpr int PER = 8 / NDB;  // slice-1 elements per MFMA
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          mma_a(dq[mb][db], da[mb][0], bk);
-#pragma unroll
-          for (int k = 0; k < PER; ++k) {
-            const int e = (db * MB + mb) * PER + k;  // 0 .. 8 MB - 1 over slice 1
-            elem(e >> 3, 8 + (e & 7));
-          }
-        }
-        bk = bk_n;
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int sl = 0; sl < 2 * NB; ++sl) {
+      const int nb = sl >> 1, ks = sl & 1;
+      const int ro = L::rows(32 * nb + 16 * ks);
+      F bk = lds_frag_tr<T>(cur, t_off[0][0] + ro, t_off[0][1] + ro);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         F bk_n;
-        if (db + 1 < NDB) bk_n = lds_frag_tr<T>(cur, t_off[db + 1][0] + L::rows(16), t_off[db + 1][1] + L::rows(16));
+        if (db + 1 < NDB) bk_n = lds_frag_tr<T>(cur, t_off[db + 1][0] + ro, t_off[db + 1][1] + ro);
+        mma_a(dq[db], da[nb][ks], bk);
+        if (sl + 1 < 2 * NB) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) mma_a(dq[mb][db], da[mb][1], bk);
+          for (int k = 0; k < PER; ++k) elem((sl + 1) >> 1, 8 * ((sl + 1) & 1) + db * PER + k);
+        }
         if (db + 1 < NDB) bk = bk_n;
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
 
-  int cb = 0;
+  int cb = 0;  // buffer of step j
   for (int j = 0; j < j_end; ++j) {
-    const int nb2 = cb >= 1 ? cb - 1 : 2;
-    step_body(smem + cb * C::BUF, smem + nb2 * C::BUF, j);
-    wait_vm_le<C::ISSUE>();  // tile j + 1 has landed; tile j + 2 may stay in flight
+    const int pb = cb == 0 ? STAGES - 1 : cb - 1;  // (j + STAGES - 1) % STAGES
+    step_body(smem + cb * C::BUF, smem + pb * C::BUF, j);
+    wait_vm_le<C::ISSUE * (STAGES - 2)>();  // tile j + 1 has landed
     barrier_lds();
-    cb = cb == 2 ? 0 : cb + 1;
+    cb = cb == STAGES - 1 ? 0 : cb + 1;
   }
   wait_vm_all();  // no prefetch may still be writing LDS when the workgroup ends
 
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) mma_drain(dq[mb]);
+  mma_drain(dq);
   T* dQg = (T*)p.dq + q_off * HD;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = mw0 + 32 * mb + 8 * (r >> 2) + 4 * hl + (r & 3);
-        if (m < Sq) dQg[(size_t)m * HD + 32 * db + c32] = (T)(dq[mb][db][r] * p.scale);
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int mr = mw0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+      if (mr < Sq) dQg[(size_t)mr * HD + 32 * db + c32] = (T)(dq[db][r] * p.scale);
+    }
 }
 
 template <class T, int HD>
@@ -658,22 +643,21 @@ static hipError_t go_dkdv(const BwdParams& p, hipStream_t s, LaunchInfo* info) {
   return hipGetLastError();
 }
 
-// 32-row blocks per wave of the dQ kernel.  1 (128-row workgroups, two per CU, two waves per
-// SIMD) measured 5 % faster than 2 (256-row workgroups, one wave per SIMD) on the headline
-// shape: the second wave on a SIMD issues while the first waits, which outweighs reading
-// the K and V fragments twice as often from LDS.
-#ifndef FAB_DQ_MB
-#define FAB_DQ_MB 1
+// Key blocks of 32 per step of the dQ kernel (1: 32-key steps through a three-stage ring;
+// 2: 64-key steps through a double buffer, which pays the per-step barrier, waits and
+// scalar bookkeeping half as often and measures 2% faster at head dim 128).
+#ifndef FAB_DQ_NB
+#define FAB_DQ_NB 2
 #endif
-constexpr int kDqMB = FAB_DQ_MB;
+constexpr int kDqNB = FAB_DQ_NB;
 
 template <class T, int HD>
 static hipError_t go_dq(const BwdParams& p, hipStream_t s, LaunchInfo* info) {
-  typedef Dq16<HD, kDqMB> C;
+  typedef Dq16<HD, kDqNB> C;
   const int n_qt = (p.Sq + C::BM - 1) / C::BM;
   const int grid = p.n_units * (p.H / p.H_kv) * n_qt;
   if (info) *info = LaunchInfo{"bwd_dq16", grid, 256, C::LDS};
-  hipLaunchKernelGGL((bwd_dq16_kernel<T, HD, kDqMB>), dim3(grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((bwd_dq16_kernel<T, HD, kDqNB>), dim3(grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

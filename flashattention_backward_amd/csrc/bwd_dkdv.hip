@@ -1,3 +1,6 @@
+// fp32 inputs only (v_mfma_f32_32x32x2f32: fp32 products and sums); bf16 and fp16 inputs use
+// the tiled kernels of bwd16.hip.
+//
 // Main backward step for dK and dV (boostr flash_bwd.rs, "Step 2: Main backward kernel",
 // whose launch gives every workgroup one tile of keys: grid (batch*heads, ceil(Sk/BLOCK_N))
 // with K, V, Q and dO tiles in shared memory).
@@ -211,8 +214,7 @@ static hipError_t go(const BwdParams& p, hipStream_t s, LaunchInfo* info) {
 }
 
 hipError_t launch_bwd_dkdv(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info) {
-  if (dt == kBF16) return hd == 64 ? go<bf16, 64>(p, s, info) : go<bf16, 128>(p, s, info);
-  if (dt == kF16) return hd == 64 ? go<f16, 64>(p, s, info) : go<f16, 128>(p, s, info);
+  (void)dt;  // fp32 only: the 16-bit inputs have their own tiled kernels
   return hd == 64 ? go<float, 64>(p, s, info) : go<float, 128>(p, s, info);
 }
 

@@ -1,3 +1,6 @@
+// fp32 inputs only (v_mfma_f32_32x32x2f32: fp32 products and sums); bf16 and fp16 inputs use
+// the tiled kernels of bwd16.hip.
+//
 // Main backward step for dQ, query-tile outer (the dQ pass of rustytorch's
 // rtx-flash-metal-attention backward.rs, which dispatches one threadgroup per block of
 // queries per (batch, head)).  A workgroup owns BM = 128 query rows of one (batch, head);
@@ -186,8 +189,7 @@ static hipError_t go(const BwdParams& p, hipStream_t s, LaunchInfo* info) {
 }
 
 hipError_t launch_bwd_dq(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info) {
-  if (dt == kBF16) return hd == 64 ? go<bf16, 64>(p, s, info) : go<bf16, 128>(p, s, info);
-  if (dt == kF16) return hd == 64 ? go<f16, 64>(p, s, info) : go<f16, 128>(p, s, info);
+  (void)dt;  // fp32 only: the 16-bit inputs have their own tiled kernels
   return hd == 64 ? go<float, 64>(p, s, info) : go<float, 128>(p, s, info);
 }
 

@@ -1,3 +1,6 @@
+// fp32 inputs only (v_mfma_f32_32x32x2f32: fp32 products and sums); bf16 and fp16 inputs use
+// the tiled forward of fwd16.hip.
+//
 // Supporting forward: O = softmax(scale Q K^T over the allowed keys) V and the row LSE
 // (natural log), which the backward consumes (boostr autograd_attention.rs,
 // var_flash_attention: the forward returns (output, lse) and the lse stays internal to the
@@ -198,8 +201,7 @@ static hipError_t go(const FwdParams& p, hipStream_t s, LaunchInfo* info) {
 }
 
 hipError_t launch_fwd(const FwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info) {
-  if (dt == kBF16) return hd == 64 ? go<bf16, 64>(p, s, info) : go<bf16, 128>(p, s, info);
-  if (dt == kF16) return hd == 64 ? go<f16, 64>(p, s, info) : go<f16, 128>(p, s, info);
+  (void)dt;  // fp32 only: the 16-bit inputs have their own tiled kernels
   return hd == 64 ? go<float, 64>(p, s, info) : go<float, 128>(p, s, info);
 }
 
