@@ -23,6 +23,14 @@ Readings where the pages are silent (each also listed in the design notes):
 
 * LSE is the natural-log log-sum-exp of the scaled scores.
 * Causal masking is top-left aligned: query i may attend key j iff j <= i.
+* Sliding window.  The autograd_attention.rs page passes a ``window_size`` to both the
+  forward and the backward, and flash_bwd.rs's backward rejects any value but 0; neither
+  page says what the window keeps.  Read here as: W > 0 keeps W keys per query row i, the
+  keys j with i - W < j (the W most recent ones, i itself included, under the causal mask)
+  and, without the causal mask, also j < i + W; W = 0 is no window.
+* A row with no allowed key (only possible with a window and Sq - Sk >= W) has the empty
+  sum's LSE = log 0 = -inf and O = 0; P and dS are 0 on it, so its dQ is 0 and it adds
+  nothing to dK, dV.
 * Grouped-query heads are contiguous: query head h uses kv head h // (H / H_kv), and dK, dV
   sum the contributions of all query heads of a group.
 * dQ and dK carry the factor ``scale`` (the gradient of the function actually computed).
@@ -41,12 +49,21 @@ def kv_head_of(h: int, H: int, H_kv: int) -> int:
     return h // (H // H_kv)
 
 
-def allowed_mask(rows: np.ndarray, Sk: int, causal: bool) -> np.ndarray:
-    """Boolean [len(rows), Sk]: True where query row i may attend key j (top-left causal)."""
-    cols = np.arange(Sk)
-    if not causal:
-        return np.ones((len(rows), Sk), dtype=bool)
-    return cols[None, :] <= rows[:, None]
+def allowed_mask(rows: np.ndarray, Sk: int, causal: bool, window: int = 0) -> np.ndarray:
+    """Boolean [len(rows), Sk]: True where query row i may attend key j (top-left causal;
+    with window W > 0 also i - W < j, and j < i + W when not causal)."""
+    if window < 0:
+        raise ValueError("window must be >= 0")
+    i = np.asarray(rows)[:, None]
+    j = np.arange(Sk)[None, :]
+    ok = np.ones((len(rows), Sk), dtype=bool)
+    if causal:
+        ok &= j <= i
+    if window > 0:
+        ok &= j > i - window
+        if not causal:
+            ok &= j < i + window
+    return ok
 
 
 def _as64(x) -> np.ndarray:
@@ -67,8 +84,10 @@ def _check_shapes(q, k, v):
     return B, H, H_kv, Sq, k.shape[2], D
 
 
-def attention_forward(q, k, v, causal: bool, scale: float, heads=None, row_block: int = ROW_BLOCK):
+def attention_forward(q, k, v, causal: bool, scale: float, heads=None, row_block: int = ROW_BLOCK,
+                      window: int = 0):
     """O = softmax(scale Q K^T restricted to allowed keys) V and the row LSE (natural log).
+    A row with no allowed key gets O = 0 and LSE = -inf.
 
     ``heads``: optional iterable of (b, h) pairs to compute; other rows are left as NaN.
     Returns (O [B,H,Sq,D] float64, LSE [B,H,Sq] float64).
@@ -83,19 +102,21 @@ def attention_forward(q, k, v, causal: bool, scale: float, heads=None, row_block
         for i0 in range(0, Sq, row_block):
             rows = np.arange(i0, min(Sq, i0 + row_block))
             s = scale * (q[b, h, rows] @ k[b, g].T)                 # scaled scores
-            ok = allowed_mask(rows, Sk, causal)
+            ok = allowed_mask(rows, Sk, causal, window)
             s = np.where(ok, s, -np.inf)
-            m = s.max(axis=1, keepdims=True)                         # every row has key 0
-            l = np.exp(s - m).sum(axis=1, keepdims=True)
-            row_lse = m + np.log(l)
-            p = np.exp(s - row_lse)                                  # masked entries: exp(-inf) = 0
+            has = ok.any(axis=1, keepdims=True)                      # rows with >= 1 key
+            m = np.where(has, s.max(axis=1, keepdims=True), 0.0)
+            l = np.exp(s - m).sum(axis=1, keepdims=True)             # 0 for a row with no key
+            with np.errstate(divide="ignore"):
+                row_lse = m + np.log(l)                              # log 0 = -inf there
+            p = np.where(ok, np.exp(np.where(ok, s, 0.0) - np.where(has, row_lse, 0.0)), 0.0)
             o[b, h, rows] = p @ v[b, g]
             lse[b, h, rows] = row_lse[:, 0]
     return o, lse
 
 
 def attention_backward(do, q, k, v, o, lse, causal: bool, scale: float, groups=None,
-                       row_block: int = ROW_BLOCK):
+                       row_block: int = ROW_BLOCK, window: int = 0):
     """The two-step backward: D = rowsum(dO * O), then dQ, dK, dV from P recomputed via LSE.
 
     ``groups``: optional iterable of (b, g) kv-head groups to compute; rows of other groups
@@ -117,9 +138,11 @@ def attention_backward(do, q, k, v, o, lse, causal: bool, scale: float, groups=N
         for h in range(g * G, (g + 1) * G):
             for i0 in range(0, Sq, row_block):
                 rows = np.arange(i0, min(Sq, i0 + row_block))
-                ok = allowed_mask(rows, Sk, causal)
+                ok = allowed_mask(rows, Sk, causal, window)
                 s = scale * (q[b, h, rows] @ k[b, g].T)
-                p = np.where(ok, np.exp(s - lse[b, h, rows][:, None]), 0.0)
+                # P on allowed pairs only; a row with no allowed key (LSE = -inf) is all zero
+                lse_r = lse[b, h, rows][:, None]
+                p = np.where(ok, np.exp(np.where(ok, s - lse_r, 0.0)), 0.0)
                 dp = do[b, h, rows] @ v[b, g].T
                 ds = p * (dp - delta[b, h, rows][:, None])
                 dv[b, g] += p.T @ do[b, h, rows]
@@ -128,7 +151,7 @@ def attention_backward(do, q, k, v, o, lse, causal: bool, scale: float, groups=N
     return dq, dk, dv, delta
 
 
-def attention_grads(q, k, v, do, causal: bool, scale: float, groups=None):
+def attention_grads(q, k, v, do, causal: bool, scale: float, groups=None, window: int = 0):
     """Forward then backward on the same inputs (the end-to-end comparison).
 
     Returns a dict with o, lse, dq, dk, dv, delta (float64).  With ``groups`` only the
@@ -141,29 +164,30 @@ def attention_grads(q, k, v, do, causal: bool, scale: float, groups=None):
     if groups is not None:
         groups = list(groups)
         heads = [(b, h) for b, g in groups for h in range(g * G, (g + 1) * G)]
-    o, lse = attention_forward(q64, k64, v64, causal, scale, heads=heads)
+    o, lse = attention_forward(q64, k64, v64, causal, scale, heads=heads, window=window)
     if heads is not None:
         # rows outside the requested groups stay NaN; give the backward finite placeholders
-        o = np.nan_to_num(o)
-        lse = np.nan_to_num(lse)
+        o = np.where(np.isnan(o), 0.0, o)
+        lse = np.where(np.isnan(lse), 0.0, lse)
     dq, dk, dv, delta = attention_backward(do64, q64, k64, v64, o, lse, causal, scale,
-                                           groups=groups)
+                                           groups=groups, window=window)
     return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "delta": delta}
 
 
 def _worker(args):
-    q, k, v, do, causal, scale, group = args
+    q, k, v, do, causal, scale, group, window = args
     from threadpoolctl import threadpool_limits
     with threadpool_limits(1):
-        return group, attention_grads(q, k, v, do, causal, scale, groups=[group])
+        return group, attention_grads(q, k, v, do, causal, scale, groups=[group], window=window)
 
 
 def _serial(args):
-    q, k, v, do, causal, scale, group = args
-    return group, attention_grads(q, k, v, do, causal, scale, groups=[group])
+    q, k, v, do, causal, scale, group, window = args
+    return group, attention_grads(q, k, v, do, causal, scale, groups=[group], window=window)
 
 
-def grads_for_groups(q, k, v, do, causal: bool, scale: float, groups, jobs: int = 1):
+def grads_for_groups(q, k, v, do, causal: bool, scale: float, groups, jobs: int = 1,
+                     window: int = 0):
     """attention_grads over several (b, g) groups, optionally in a process pool.
 
     With jobs > 1 each worker process receives only its group's slices and uses one BLAS
@@ -178,7 +202,7 @@ def grads_for_groups(q, k, v, do, causal: bool, scale: float, groups, jobs: int 
     for b, g in groups:
         hs = slice(g * G, (g + 1) * G)
         tasks.append((q64[b:b + 1, hs], k64[b:b + 1, g:g + 1], v64[b:b + 1, g:g + 1],
-                      do64[b:b + 1, hs], causal, scale, (0, 0)))
+                      do64[b:b + 1, hs], causal, scale, (0, 0), window))
     if jobs <= 1:
         outs = [_serial(t)[1] for t in tasks]  # one process, BLAS threads as configured
     else:
