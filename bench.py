@@ -49,8 +49,7 @@ KERNEL_SOURCE = {"bwd_dkdv": "bwd16.hip", "bwd_dq": "bwd16.hip", "preprocess": "
 
 
 def allowed_pairs(w) -> float:
-    p = float(w.B) * w.H * w.Sq * w.Sk
-    return p / 2 if w.causal else p
+    return w.allowed_pairs()
 
 
 def source_digest(kernel: str) -> str:
@@ -142,7 +141,8 @@ class Bwd:
         self.w, self.fab, self.L = w, fab, fab.lib()
         dev = torch.device("cuda:0")
         self.q, self.k, self.v, self.do = (x.to(dev) for x in (q, k, v, do))
-        self.o, self.lse = fab.fwd(self.q, self.k, self.v, causal=w.causal, scale=w.scale)
+        self.o, self.lse = fab.fwd(self.q, self.k, self.v, causal=w.causal, scale=w.scale,
+                                   window_size=w.window)
         self.dq = torch.empty_like(self.q)
         self.dk = torch.empty_like(self.k)
         self.dv = torch.empty_like(self.v)
@@ -150,7 +150,8 @@ class Bwd:
         nb = fab.bwd_workspace_bytes(w.B, w.H, w.H_kv, w.Sq, w.Sk, w.D, self.code)
         self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
         self.stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-        self.dims = (w.B, w.H, w.H_kv, w.Sq, w.Sk, w.D, self.code, int(w.causal), float(w.scale))
+        self.dims = (w.B, w.H, w.H_kv, w.Sq, w.Sk, w.D, self.code, int(w.causal), w.window,
+                     float(w.scale))
         torch.cuda.synchronize()
 
     def _ok(self, st):
@@ -168,7 +169,7 @@ class Bwd:
         w = self.w
         self._ok(self.L.fab_fwd(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),
                                 self.o.data_ptr(), self.lse.data_ptr(), w.B, w.H, w.H_kv, w.Sq, w.Sk,
-                                w.D, self.code, int(w.causal), float(w.scale), self.stream))
+                                w.D, self.code, int(w.causal), w.window, float(w.scale), self.stream))
 
     def preprocess(self):
         w = self.w

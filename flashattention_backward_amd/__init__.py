@@ -55,15 +55,15 @@ def lib() -> ctypes.CDLL:
             L.fab_bwd_workspace_bytes.restype = sz
             L.fab_bwd_workspace_bytes.argtypes = [i] * 7
             L.fab_fwd.restype = i
-            L.fab_fwd.argtypes = [vp] * 5 + [i] * 7 + [i, f, vp]
+            L.fab_fwd.argtypes = [vp] * 5 + [i] * 7 + [i, i, f, vp]
             L.fab_bwd_preprocess.restype = i
             L.fab_bwd_preprocess.argtypes = [vp] * 4 + [sz] + [i] * 5 + [vp]
             L.fab_bwd.restype = i
-            L.fab_bwd.argtypes = [vp] * 10 + [sz] + [i] * 7 + [i, f, vp]
+            L.fab_bwd.argtypes = [vp] * 10 + [sz] + [i] * 7 + [i, i, f, vp]
             L.fab_bwd_dkdv.restype = i
-            L.fab_bwd_dkdv.argtypes = [vp] * 5 + [sz] + [vp] * 2 + [i] * 7 + [i, f, vp]
+            L.fab_bwd_dkdv.argtypes = [vp] * 5 + [sz] + [vp] * 2 + [i] * 7 + [i, i, f, vp]
             L.fab_bwd_dq.restype = i
-            L.fab_bwd_dq.argtypes = [vp] * 5 + [sz] + [vp] + [i] * 7 + [i, f, vp]
+            L.fab_bwd_dq.argtypes = [vp] * 5 + [sz] + [vp] + [i] * 7 + [i, i, f, vp]
             _lib = L
     return _lib
 
@@ -105,8 +105,17 @@ def bwd_workspace_bytes(B, H, H_kv, Sq, Sk, D, dtype_code) -> int:
     return int(lib().fab_bwd_workspace_bytes(B, H, H_kv, Sq, Sk, D, dtype_code))
 
 
-def fwd(q, k, v, causal: bool = False, scale: float | None = None):
-    """Supporting forward: returns (o [B,H,Sq,D] in q's dtype, lse [B,H,Sq] float32)."""
+def _window(window_size) -> int:
+    w = int(window_size)
+    _require(w >= 0, "window_size", f"{w} is negative (0 = no window)")
+    return min(w, 2**31 - 1)
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, window_size: int = 0):
+    """Supporting forward: returns (o [B,H,Sq,D] in q's dtype, lse [B,H,Sq] float32).
+
+    window_size = W > 0 keeps W keys per query row i: keys j > i - W (and j < i + W without
+    the causal mask).  A row left without keys gets o = 0 and lse = -inf."""
     import torch
     _require(q.dim() == 4, "q", f"must be 4-D [B, H, Sq, D], got {tuple(q.shape)}")
     _require(k.dim() == 4, "k", f"must be 4-D [B, H_kv, Sk, D], got {tuple(k.shape)}")
@@ -121,8 +130,8 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None):
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
     _check(lib().fab_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                         B, H, H_kv, Sq, Sk, D, _dtype_code(q), int(bool(causal)), float(scale),
-                         _stream_handle(dev)))
+                         B, H, H_kv, Sq, Sk, D, _dtype_code(q), int(bool(causal)),
+                         _window(window_size), float(scale), _stream_handle(dev)))
     return o, lse
 
 
@@ -150,8 +159,9 @@ def bwd_preprocess(do, o, lse):
 
 
 def bwd(do, q, k, v, o, lse, num_heads: int | None = None, num_kv_heads: int | None = None,
-        causal: bool = False, scale: float | None = None, workspace=None):
-    """The backward: returns (dq, dk, dv) with the shapes and dtype of (q, k, v)."""
+        causal: bool = False, scale: float | None = None, workspace=None, window_size: int = 0):
+    """The backward: returns (dq, dk, dv) with the shapes and dtype of (q, k, v).  `causal`,
+    `scale` and `window_size` must be those the forward ran with."""
     import torch
     _require(q.dim() == 4, "q", f"must be 4-D [B, H, Sq, D], got {tuple(q.shape)}")
     _require(k.dim() == 4, "k", f"must be 4-D [B, H_kv, Sk, D], got {tuple(k.shape)}")
@@ -183,6 +193,6 @@ def bwd(do, q, k, v, o, lse, num_heads: int | None = None, num_kv_heads: int | N
     _check(lib().fab_bwd(do.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                          lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                         B, H, H_kv, Sq, Sk, D, code, int(bool(causal)), float(scale),
-                         _stream_handle(dev)))
+                         B, H, H_kv, Sq, Sk, D, code, int(bool(causal)), _window(window_size),
+                         float(scale), _stream_handle(dev)))
     return dq, dk, dv

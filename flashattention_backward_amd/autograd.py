@@ -21,11 +21,12 @@ __all__ = ["FlashAttention", "flash_attention"]
 
 class FlashAttention(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, causal: bool, scale, return_lse: bool):
-        o, lse = fwd(q, k, v, causal=causal, scale=scale)
+    def forward(ctx, q, k, v, causal: bool, scale, return_lse: bool, window_size: int):
+        o, lse = fwd(q, k, v, causal=causal, scale=scale, window_size=window_size)
         ctx.save_for_backward(q, k, v, o, lse)
         ctx.causal = bool(causal)
         ctx.scale = scale
+        ctx.window_size = int(window_size)
         if return_lse:
             ctx.mark_non_differentiable(lse)
             return o, lse
@@ -35,12 +36,14 @@ class FlashAttention(torch.autograd.Function):
     @torch.autograd.function.once_differentiable
     def backward(ctx, do, *unused):
         q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = bwd(do.contiguous(), q, k, v, o, lse, causal=ctx.causal, scale=ctx.scale)
-        return dq, dk, dv, None, None, None
+        dq, dk, dv = bwd(do.contiguous(), q, k, v, o, lse, causal=ctx.causal, scale=ctx.scale,
+                         window_size=ctx.window_size)
+        return dq, dk, dv, None, None, None, None
 
 
 def flash_attention(q, k, v, causal: bool = False, scale: float | None = None,
-                    return_lse: bool = False):
+                    return_lse: bool = False, window_size: int = 0):
     """Attention output [B, H, Sq, D] (and its lse [B, H, Sq] if ``return_lse``), with
-    gradients through the HIP backward.  Layouts and dtypes as for ``fwd``."""
-    return FlashAttention.apply(q, k, v, causal, scale, return_lse)
+    gradients through the HIP backward.  Layouts, dtypes and ``window_size`` as for ``fwd``
+    (the configuration autograd_attention.rs saves for the backward: causal and window)."""
+    return FlashAttention.apply(q, k, v, causal, scale, return_lse, window_size)

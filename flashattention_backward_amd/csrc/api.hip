@@ -118,14 +118,28 @@ size_t ws_bytes(long long B, long long H, long long Sq) {
 
 int units_per_xcd(int n_units) { return n_units % 8 == 0 ? n_units / 8 : 0; }
 
+fab_status check_window(int window_size) {
+  if (window_size < 0)
+    return fail(FAB_ERR_INVALID_ARGUMENT, "window_size", "%d is negative (0 = no window)", window_size);
+  return FAB_OK;
+}
+
+// The window as the kernels take it: 0 for none, and also for a window of at least
+// max(Sq, Sk) keys, which cuts no (query, key) pair of these sizes.
+int kernel_window(int window_size, int Sq, int Sk) {
+  return window_size >= (Sq > Sk ? Sq : Sk) ? 0 : window_size;
+}
+
 fab::BwdParams bwd_params(const void* dO, const void* q, const void* k, const void* v,
                           const void* workspace, void* dq, void* dk, void* dv,
-                          int B, int H, int H_kv, int Sq, int Sk, int causal, float scale) {
+                          int B, int H, int H_kv, int Sq, int Sk, int causal, int window_size,
+                          float scale) {
   fab::BwdParams p;
   p.q = q; p.k = k; p.v = v; p.dO = dO; p.stats = static_cast<const float*>(workspace);
   p.dq = dq; p.dk = dk; p.dv = dv;
   p.B = B; p.H = H; p.H_kv = H_kv; p.Sq = Sq; p.Sk = Sk; p.Sq_pad = fab::stats_rows(Sq);
   p.causal = causal ? 1 : 0;
+  p.win = kernel_window(window_size, Sq, Sk);
   p.scale = scale;
   // The kernels mask a score by replacing it with mask_s, for which mask_s * scale_log2 is
   // -inf.  A zero (or subnormal) exponent scale is raised to the smallest normal float of the
@@ -142,8 +156,10 @@ fab::BwdParams bwd_params(const void* dO, const void* q, const void* k, const vo
 
 // Checks shared by fab_bwd and the two step-2 entry points (every pointer but dq/dk/dv).
 fab_status check_bwd_inputs(const void* dO, const void* q, const void* k, const void* v,
-                            int B, int H, int H_kv, int Sq, int Sk, int D, int dtype, float scale) {
+                            int B, int H, int H_kv, int Sq, int Sk, int D, int dtype,
+                            int window_size, float scale) {
   FAB_TRY(check_common(B, H, H_kv, Sq, Sk, D, dtype));
+  FAB_TRY(check_window(window_size));
   FAB_TRY(check_ptr(dO, "dO"));
   FAB_TRY(check_ptr(q, "q"));
   FAB_TRY(check_ptr(k, "k"));
@@ -217,8 +233,9 @@ size_t fab_bwd_workspace_bytes(int B, int H, int H_kv, int Sq, int Sk, int D, in
 
 fab_status fab_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int H_kv, int Sq, int Sk, int D, int dtype,
-                   int causal, float scale, void* stream) {
+                   int causal, int window_size, float scale, void* stream) {
   FAB_TRY(check_common(B, H, H_kv, Sq, Sk, D, dtype));
+  FAB_TRY(check_window(window_size));
   FAB_TRY(check_ptr(q, "q"));
   FAB_TRY(check_ptr(k, "k"));
   FAB_TRY(check_ptr(v, "v"));
@@ -237,6 +254,7 @@ fab_status fab_fwd(const void* q, const void* k, const void* v, void* o, float* 
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.B = B; p.H = H; p.H_kv = H_kv; p.Sq = Sq; p.Sk = Sk;
   p.causal = causal ? 1 : 0;
+  p.win = kernel_window(window_size, Sq, Sk);
   p.scale = scale;
   p.scale_log2 = scale * fab::kLog2eHost;
   p.n_units = B * H_kv;
@@ -273,8 +291,8 @@ fab_status fab_bwd(const void* dO, const void* q, const void* k, const void* v,
                    const void* o, const float* lse, void* dq, void* dk, void* dv,
                    void* workspace, size_t workspace_bytes,
                    int B, int H, int H_kv, int Sq, int Sk, int D, int dtype,
-                   int causal, float scale, void* stream) {
-  FAB_TRY(check_bwd_inputs(dO, q, k, v, B, H, H_kv, Sq, Sk, D, dtype, scale));
+                   int causal, int window_size, float scale, void* stream) {
+  FAB_TRY(check_bwd_inputs(dO, q, k, v, B, H, H_kv, Sq, Sk, D, dtype, window_size, scale));
   FAB_TRY(check_ptr(o, "o"));
   FAB_TRY(check_ptr(lse, "lse"));
   FAB_TRY(check_ptr(dq, "dq"));
@@ -296,7 +314,8 @@ fab_status fab_bwd(const void* dO, const void* q, const void* k, const void* v,
   const fab::PreParams pp = pre_params(dO, o, lse, workspace, B, H, Sq);
   FAB_TRY(launched(fab::launch_preprocess(pp, dtype, D, s, &li), "preprocess"));
   log_launch(li);
-  const fab::BwdParams p = bwd_params(dO, q, k, v, workspace, dq, dk, dv, B, H, H_kv, Sq, Sk, causal, scale);
+  const fab::BwdParams p =
+      bwd_params(dO, q, k, v, workspace, dq, dk, dv, B, H, H_kv, Sq, Sk, causal, window_size, scale);
   FAB_TRY(launched(launch_step2(p, dtype, D, s, true, true, &li), "step 2"));
   return FAB_OK;
 }
@@ -304,8 +323,8 @@ fab_status fab_bwd(const void* dO, const void* q, const void* k, const void* v,
 fab_status fab_bwd_dkdv(const void* dO, const void* q, const void* k, const void* v,
                         const void* workspace, size_t workspace_bytes, void* dk, void* dv,
                         int B, int H, int H_kv, int Sq, int Sk, int D,
-                        int dtype, int causal, float scale, void* stream) {
-  FAB_TRY(check_bwd_inputs(dO, q, k, v, B, H, H_kv, Sq, Sk, D, dtype, scale));
+                        int dtype, int causal, int window_size, float scale, void* stream) {
+  FAB_TRY(check_bwd_inputs(dO, q, k, v, B, H, H_kv, Sq, Sk, D, dtype, window_size, scale));
   FAB_TRY(check_ptr(dk, "dk"));
   FAB_TRY(check_ptr(dv, "dv"));
   FAB_TRY(check_workspace(workspace, workspace_bytes, B, H, Sq));
@@ -314,7 +333,8 @@ fab_status fab_bwd_dkdv(const void* dO, const void* q, const void* k, const void
   FAB_TRY(check_device_range(workspace, ws_bytes(B, H, Sq), "workspace"));
   FAB_TRY(check_device_range(dk, nk, "dk"));
   FAB_TRY(check_device_range(dv, nk, "dv"));
-  const fab::BwdParams p = bwd_params(dO, q, k, v, workspace, nullptr, dk, dv, B, H, H_kv, Sq, Sk, causal, scale);
+  const fab::BwdParams p =
+      bwd_params(dO, q, k, v, workspace, nullptr, dk, dv, B, H, H_kv, Sq, Sk, causal, window_size, scale);
   fab::LaunchInfo li;
   FAB_TRY(launched(launch_step2(p, dtype, D, (hipStream_t)stream, true, false, &li), "bwd_dkdv"));
   return FAB_OK;
@@ -323,15 +343,16 @@ fab_status fab_bwd_dkdv(const void* dO, const void* q, const void* k, const void
 fab_status fab_bwd_dq(const void* dO, const void* q, const void* k, const void* v,
                       const void* workspace, size_t workspace_bytes, void* dq,
                       int B, int H, int H_kv, int Sq, int Sk, int D,
-                      int dtype, int causal, float scale, void* stream) {
-  FAB_TRY(check_bwd_inputs(dO, q, k, v, B, H, H_kv, Sq, Sk, D, dtype, scale));
+                      int dtype, int causal, int window_size, float scale, void* stream) {
+  FAB_TRY(check_bwd_inputs(dO, q, k, v, B, H, H_kv, Sq, Sk, D, dtype, window_size, scale));
   FAB_TRY(check_ptr(dq, "dq"));
   FAB_TRY(check_workspace(workspace, workspace_bytes, B, H, Sq));
   const size_t nq = (size_t)B * H * Sq * D * elem_size(dtype);
   FAB_TRY(check_bwd_device(dO, q, k, v, B, H, H_kv, Sq, Sk, D, dtype));
   FAB_TRY(check_device_range(workspace, ws_bytes(B, H, Sq), "workspace"));
   FAB_TRY(check_device_range(dq, nq, "dq"));
-  const fab::BwdParams p = bwd_params(dO, q, k, v, workspace, dq, nullptr, nullptr, B, H, H_kv, Sq, Sk, causal, scale);
+  const fab::BwdParams p =
+      bwd_params(dO, q, k, v, workspace, dq, nullptr, nullptr, B, H, H_kv, Sq, Sk, causal, window_size, scale);
   fab::LaunchInfo li;
   FAB_TRY(launched(launch_step2(p, dtype, D, (hipStream_t)stream, false, true, &li), "bwd_dq"));
   return FAB_OK;

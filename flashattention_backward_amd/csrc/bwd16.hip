@@ -74,7 +74,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   const int n0 = wi.step * BN;
   const int G = p.H / p.H_kv;
   const int Sq = p.Sq, Sk = p.Sk, Sq_pad = p.Sq_pad;
-  const bool causal = p.causal != 0;
   const size_t kv_off = (size_t)(b * p.H_kv + g) * Sk * HD;
   const T* Kg = (const T*)p.k + kv_off;
   const T* Vg = (const T*)p.v + kv_off;
@@ -120,15 +119,23 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   // plus a wave constant.
   const char* const vrows = vtile + L::rows(64 * kb) - L::rows(32 * qh);
 
-  // ---- iteration space: every query head of the group and every query tile whose rows
-  // the causal mask lets reach these keys.  Tiles run from the last one down, heads inside:
-  // step s is tile n_qt - 1 - s / G of head s % G.  Every key tile's sequence starts at the
-  // same (tile, head), so the workgroups of a group that run together on an XCD read the
-  // same Q and dO tile at about the same time and share it through that XCD's L2.
+  // ---- iteration space: every query head of the group and every query tile holding a row
+  // that may attend one of these keys (rows [r_lo, r_hi]).  Tiles run from the last one
+  // down, heads inside: step s is tile i_last - s / G of head s % G.  Without a window every
+  // key tile's sequence starts at the same (tile, head), so the workgroups of a group that
+  // run together on an XCD read the same Q and dO tile at about the same time and share it
+  // through that XCD's L2.
   const int n_qt = (Sq + BM - 1) / BM;
-  const int i_first = causal ? min(n0 / BM, n_qt) : 0;
-  const int per = n_qt - i_first;
+  const KeyRange kr{Sk, p.causal, p.win};
+  const int r_lo = max(kr.rows_lo(n0), 0), r_hi = min(kr.rows_hi(min(n0 + BN, Sk) - 1), Sq - 1);
+  const int i_first = r_lo / BM, i_last = r_hi / BM;
+  const int per = r_hi >= r_lo ? i_last - i_first + 1 : 0;
   const int total = G * per;
+  // The wave's 32 rows from mw0 see all of its 64 keys from nw0 iff kr.hi(mw0) >= nw0 + 63
+  // and kr.lo(mw0 + 31) <= nw0, i.e. iff full_lo <= mw0 <= full_hi:
+  const int full_lo = nw0 + 63 > Sk - 1 ? (1 << 30)
+                      : p.causal ? nw0 + 63 : (p.win > 0 ? nw0 + 64 - p.win : -(1 << 30));
+  const int full_hi = p.win > 0 ? nw0 + p.win - 32 : (1 << 30);
 
   // Buffer resources over the rows of the group's query heads (Q, dO) and their row
   // statistics.  A tile is selected by a uniform byte offset; rows past a head's end read the
@@ -146,7 +153,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   // Head and tile of the next stage to prefetch, advanced once per issued stage.  Past the
   // last step the offsets leave the group (or wrap): those reads are range-checked zeros or
   // in-range rows, landing in a stage nothing reads.
-  int ph = 0, pit = n_qt - 1;
+  int ph = 0, pit = i_last;
   auto issue_part = [&](char* buf, int k, unsigned q_soff, unsigned st_soff) {
     qdma.issue(k, buf, rq, q_soff, spare, lane);
     qdma.issue(k, buf + C::TILE, rdo, q_soff, spare, lane);
@@ -241,20 +248,21 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // Masking, only on steps that need it (the causal diagonal, the last key tile): a cut
-    // score is replaced by mask_s, whose exponent is -inf, so P = 0 and dS = 0 there.  Key n
-    // (this lane's column of block nb) may be seen by row m iff n < Sk and (not causal or
-    // n <= m).
-    if ((n0 + BN > Sk) || (causal && nw0 + 63 > mw0)) {
+    // Masking, only on steps that cut some row's keys (the causal diagonal, a window's
+    // edges, the last key tile): a cut score is replaced by mask_s, whose exponent is -inf,
+    // so P = 0 and dS = 0 there.  Key n (this lane's column of block nb) may be seen by the
+    // rows [kr.rows_lo(n), kr.rows_hi(n)] if n < Sk; register r holds row m_base + off(r).
+    if (mw0 < full_lo || mw0 > full_hi) {
       const int m_base = mw0 + 4 * hl;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const int n = nw0 + 32 * nb + c32;
-        const int lim = n >= Sk ? (1 << 30) : (causal ? n - m_base : -(1 << 30));
+        const int a = n < Sk ? kr.rows_lo(n) - m_base : (1 << 30);
+        const int z = kr.rows_hi(n) - m_base;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int off = 8 * (r >> 2) + (r & 3);
-          S[nb][r] = off < lim ? mask_s : S[nb][r];
+          S[nb][r] = (off >= a && off <= z) ? S[nb][r] : mask_s;
         }
       }
     }
@@ -365,7 +373,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   };
 
   int cb = 0;  // buffer of step s
-  int it = n_qt - 1, hh = 0;
+  int it = i_last, hh = 0;
   for (int s = 0; s < total; ++s) {
     const int nb1 = cb == 2 ? 0 : cb + 1;  // (s + 1) % 3
     const int nb2 = cb >= 1 ? cb - 1 : 2;  // (s + 2) % 3
@@ -519,8 +527,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(const BwdParams p) {
       t_off[db][sec] = L::off(r, col >> 3) + 2 * (col & 7);
     }
 
-  const int n_kt = (Sk + BN - 1) / BN;
-  const int j_end = causal ? min(n_kt, (min(m0 + BM, Sq) - 1) / BN + 1) : n_kt;
+  // key tiles holding a key some row of this tile may attend
+  const KeyRange kr{Sk, p.causal, p.win};
+  const int k_lo = kr.lo(m0), k_hi = kr.hi(min(m0 + BM, Sq) - 1);
+  const int j_begin = k_lo / BN;
+  const int j_end = k_hi >= k_lo ? k_hi / BN + 1 : j_begin;
 
   // K and V tiles of the kv head through buffer resources: a tile is selected by a uniform
   // byte offset, keys past Sk read as zeros (and are masked), and the prefetches issued past
@@ -537,7 +548,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(const BwdParams p) {
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
 #pragma unroll
-    for (int k = 0; k < C::KMAX; ++k) issue_part(s, smem + s * C::BUF, k);
+    for (int k = 0; k < C::KMAX; ++k) issue_part(j_begin + s, smem + s * C::BUF, k);
   wait_vm_le<C::ISSUE * (STAGES - 2)>();  // Q, dO, statistics and stage 0 have landed
   barrier_lds();
   const float mask_s = p.mask_s;
@@ -567,18 +578,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(const BwdParams p) {
     }
     __builtin_amdgcn_sched_barrier(0);
     F da[NB][2];
-    // Masking, only on steps that need it (the causal diagonal, the last key tile): a cut
-    // score is replaced by mask_s, whose exponent is -inf.  Register r of block nb holds key
-    // n0 + 32 nb + 4 hl + off(r), off = 8 (r / 4) + r % 4, of row m (one row per lane); it may
-    // be seen iff off < min(Sk, causal ? m + 1 : Sk) - n0 - 32 nb - 4 hl.
-    if ((n0 + BN > Sk) || (causal && n0 + BN - 1 > mw0)) {
+    // Masking, only on steps that cut some row's keys (the causal diagonal, a window's
+    // edges, the last key tile): a cut score is replaced by mask_s, whose exponent is -inf.
+    // Register r of block nb holds key n0 + 32 nb + 4 hl + off(r), off = 8 (r / 4) + r % 4,
+    // of row m (one row per lane); it may be seen iff kr.lo(m) <= key <= kr.hi(m).
+    if (kr.hi(mw0) < n0 + BN - 1 || kr.lo(mw0 + 31) > n0) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int lim = (causal ? min(Sk, m + 1) : Sk) - n0 - 32 * nb - 4 * hl;
+        const int base = n0 + 32 * nb + 4 * hl;
+        const int a = kr.lo(m) - base, z = kr.hi(m) - base;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int off = 8 * (r >> 2) + (r & 3);
-          St[nb][r] = off < lim ? St[nb][r] : mask_s;
+          St[nb][r] = (off >= a && off <= z) ? St[nb][r] : mask_s;
         }
       }
     }
@@ -613,7 +625,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(const BwdParams p) {
   };
 
   int cb = 0;  // buffer of step j
-  for (int j = 0; j < j_end; ++j) {
+  for (int j = j_begin; j < j_end; ++j) {
     const int pb = cb == 0 ? STAGES - 1 : cb - 1;  // (j + STAGES - 1) % STAGES
     step_body(smem + cb * C::BUF, smem + pb * C::BUF, j);
     wait_vm_le<C::ISSUE * (STAGES - 2)>();  // tile j + 1 has landed

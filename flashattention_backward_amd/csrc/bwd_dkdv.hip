@@ -63,7 +63,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p) {
   const int n0 = wi.step * BN;
   const int G = p.H / p.H_kv;
   const int Sq = p.Sq, Sk = p.Sk;
-  const bool causal = p.causal != 0;
 
   const size_t kv_off = (size_t)(b * p.H_kv + g) * Sk * HD;
   const T* Kg = (const T*)p.k + kv_off;
@@ -91,9 +90,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p) {
     dv[db] = f32x16{};
   }
 
-  const int n_qt = (Sq + BM - 1) / BM;
-  const int i_first = causal ? n0 / BM : 0;  // earlier tiles have no query row >= n0
-  const bool kv_ragged = n0 + BN > Sk;
+  // query tiles holding a row that may attend one of these keys (rows [r_lo, r_hi])
+  const KeyRange kr{Sk, p.causal, p.win};
+  const int r_lo = max(kr.rows_lo(n0), 0), r_hi = min(kr.rows_hi(min(n0 + BN, Sk) - 1), Sq - 1);
+  const int i_first = r_lo / BM;
+  const int i_end = r_hi >= r_lo ? r_hi / BM + 1 : i_first;
 
   for (int hh = 0; hh < G; ++hh) {
     const int hq = g * G + hh;
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p) {
     const T* dOg = (const T*)p.dO + q_off * HD;
     const float* Stg = p.stats + (size_t)(b * p.H + hq) * p.Sq_pad * 2;
 
-    for (int it = i_first; it < n_qt; ++it) {
+    for (int it = i_first; it < i_end; ++it) {
       const int m0 = it * BM;
       __syncthreads();  // every wave is done reading the previous tile
       {
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p) {
       __syncthreads();
 
       // Keys of this wave that no query row of the tile may attend: nothing to add.
-      if (causal && nw0 > m0 + BM - 1) continue;
+      if (kr.hi(m0 + BM - 1) < nw0 || kr.lo(m0) > nw0 + 31) continue;
 
       f32x16 S[NMB], dP[NMB];
 #pragma unroll
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p) {
         }
       }
 
-      const bool need_mask = kv_ragged || (causal && nw0 + 31 > m0);
+      const bool need_mask = kr.hi(m0) < nw0 + 31 || kr.lo(m0 + BM - 1) > nw0;
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p) {
           float pv = fast_exp2(S[mb][r] * p.scale_log2 - sL[ml]);
           if (need_mask) {
             const int mg = m0 + ml;
-            if (nrow >= Sk || (causal && nrow > mg)) pv = 0.f;
+            if (nrow < kr.lo(mg) || nrow > kr.hi(mg)) pv = 0.f;
           }
           S[mb][r] = pv;
           dP[mb][r] = pv * (dP[mb][r] - sD[ml]);

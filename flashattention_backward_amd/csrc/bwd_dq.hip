@@ -89,10 +89,13 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dq[db] = f32x16{};
 
-  const int n_kt = (Sk + BN - 1) / BN;
-  const int j_end = causal ? min(n_kt, (m0 + BM - 1) / BN + 1) : n_kt;
+  // key tiles holding a key some row of this tile may attend
+  const KeyRange kr{Sk, p.causal, p.win};
+  const int k_lo = kr.lo(m0), k_hi = kr.hi(min(m0 + BM, Sq) - 1);
+  const int j_begin = k_lo / BN;
+  const int j_end = k_hi >= k_lo ? k_hi / BN + 1 : j_begin;
 
-  for (int j = 0; j < j_end; ++j) {
+  for (int j = j_begin; j < j_end; ++j) {
     const int n0 = j * BN;
     __syncthreads();
     {
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
     }
     __syncthreads();
 
-    if (causal && n0 > mw0 + 31) continue;  // no row of this wave sees these keys
+    if (kr.hi(mw0 + 31) < n0 || kr.lo(mw0) > n0 + BN - 1) continue;  // no row of this wave sees these keys
 
     f32x16 St[NNB], dPt[NNB];
 #pragma unroll
@@ -138,7 +141,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
       }
     }
 
-    const bool need_mask = (n0 + BN > Sk) || (causal && n0 + BN - 1 > mw0);
+    const bool need_mask = kr.hi(mw0) < n0 + BN - 1 || kr.lo(mw0 + 31) > n0;
 #pragma unroll
     for (int nb = 0; nb < NNB; ++nb) {
 #pragma unroll
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
         float pv = fast_exp2(St[nb][r] * p.scale_log2 - lse2);
         if (need_mask) {
           const int n = n0 + 32 * nb + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (n >= Sk || (causal && n > m)) pv = 0.f;
+          if (n < kr.lo(m) || n > kr.hi(m)) pv = 0.f;
         }
         dPt[nb][r] = pv * (dPt[nb][r] - dl);
       }

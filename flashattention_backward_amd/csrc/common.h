@@ -383,4 +383,23 @@ __device__ __forceinline__ WorkItem map_work(int wg, int n_units, int units_per_
   return r;
 }
 
+// Keys a query row may attend (top-left indices): [lo(m), hi(m)], empty when lo > hi.
+// Every key is below Sk; with the causal mask no key is past the row itself; with a window of
+// `win` keys (win > 0) a key is more than m - win and, without the causal mask, less than
+// m + win.  win = 0 means no window (the host passes 0 for windows too wide to cut anything).
+// Both bounds are non-decreasing in m, so a block of rows [m_a, m_b] sees keys within
+// [lo(m_a), hi(m_b)], and sees every key of [n_a, n_b] iff lo(m_b) <= n_a and hi(m_a) >= n_b.
+struct KeyRange {
+  int Sk, causal, win;
+  __device__ __forceinline__ int lo(int m) const { return win > 0 ? max(m - win + 1, 0) : 0; }
+  __device__ __forceinline__ int hi(int m) const {
+    return min(Sk - 1, causal ? m : (win > 0 ? m + win - 1 : Sk - 1));
+  }
+  // Query rows that may attend key n (n < Sk), unclamped: [rows_lo(n), rows_hi(n)].
+  __device__ __forceinline__ int rows_lo(int n) const {
+    return causal ? n : (win > 0 ? n - win + 1 : -(1 << 29));
+  }
+  __device__ __forceinline__ int rows_hi(int n) const { return win > 0 ? n + win - 1 : (1 << 29); }
+};
+
 }  // namespace fab

@@ -76,10 +76,13 @@ __global__ __launch_bounds__(256) void fwd_kernel(const FwdParams p) {
   float mrun = -1e30f;  // running max of the log2-domain scores of row m (finite start)
   float lsum = 0.f;     // this lane half's share of the row sum
 
-  const int n_kt = (Sk + BN - 1) / BN;
-  const int j_end = causal ? min(n_kt, (m0 + BM - 1) / BN + 1) : n_kt;
+  // key tiles holding a key some row of this tile may attend
+  const KeyRange kr{Sk, p.causal, p.win};
+  const int k_lo = kr.lo(m0), k_hi = kr.hi(min(m0 + BM, Sq) - 1);
+  const int j_begin = k_lo / BN;
+  const int j_end = k_hi >= k_lo ? k_hi / BN + 1 : j_begin;
 
-  for (int j = 0; j < j_end; ++j) {
+  for (int j = j_begin; j < j_end; ++j) {
     const int n0 = j * BN;
     __syncthreads();
     {
@@ -108,7 +111,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(const FwdParams p) {
     }
     __syncthreads();
 
-    if (causal && n0 > mw0 + 31) continue;
+    if (kr.hi(mw0 + 31) < n0 || kr.lo(mw0) > n0 + BN - 1) continue;  // no row of this wave sees these keys
 
     f32x16 St[NNB];
 #pragma unroll
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(const FwdParams p) {
         mma(St[nb], ld8(sK + (32 * nb + c32) * LDR + 16 * c + 8 * hl), qf[c]);
     }
 
-    const bool need_mask = (n0 + BN > Sk) || (causal && n0 + BN - 1 > mw0);
+    const bool need_mask = kr.hi(mw0) < n0 + BN - 1 || kr.lo(mw0 + 31) > n0;
     float mx = -__builtin_inff();
 #pragma unroll
     for (int nb = 0; nb < NNB; ++nb) {
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(const FwdParams p) {
         float x = St[nb][r] * p.scale_log2;
         if (need_mask) {
           const int n = n0 + 32 * nb + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (n >= Sk || (causal && n > m)) x = -__builtin_inff();
+          if (n < kr.lo(m) || n > kr.hi(m)) x = -__builtin_inff();
         }
         St[nb][r] = x;
         mx = fmaxf(mx, x);
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(const FwdParams p) {
 
   const float ltot = lsum + __shfl_xor(lsum, 32);
   if (m < Sq) {
-    const float inv = 1.f / ltot;
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;  // a row with no key: O = 0, LSE = -inf
     T* Og = (T*)p.o + (q_off + m) * HD;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {

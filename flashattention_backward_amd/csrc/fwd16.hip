@@ -90,8 +90,11 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(const FwdParams p) {
       t_off[db][sec] = L::off(r, col >> 3) + 2 * (col & 7);
     }
 
-  const int n_kt = (Sk + BN - 1) / BN;
-  const int j_end = causal ? min(n_kt, (min(m0 + BM, Sq) - 1) / BN + 1) : n_kt;
+  // key tiles holding a key some row of this tile may attend
+  const KeyRange kr{Sk, p.causal, p.win};
+  const int k_lo = kr.lo(m0), k_hi = kr.hi(min(m0 + BM, Sq) - 1);
+  const int j_begin = k_lo / BN;
+  const int j_end = k_hi >= k_lo ? k_hi / BN + 1 : j_begin;
 
   TileDma<T, HD, BN> kvdma;
   kvdma.init(w, lane);
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(const FwdParams p) {
     kvdma.issue(k, buf + C::TILE, rv, (unsigned)j * TILEB, spare, lane);
   };
 #pragma unroll
-  for (int k = 0; k < C::KMAX; ++k) issue_part(0, smem, k);
+  for (int k = 0; k < C::KMAX; ++k) issue_part(j_begin, smem + (j_begin & 1) * C::BUF, k);
   wait_vm_all();
   barrier_lds();
 
@@ -133,16 +136,18 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(const FwdParams p) {
       mma(St[1], k1, qf[cc]);
     }
     // ---- scores in the log2 domain; masked ones are -inf.  Register r of block nb holds key
-    // n0 + 32 nb + 4 hl + 8 (r / 4) + r % 4 of row m.
+    // n0 + 32 nb + 4 hl + off, off = 8 (r / 4) + r % 4, of row m; it is seen iff
+    // kr.lo(m) <= key <= kr.hi(m).  Only steps that cut some row's keys test.
     const float c2 = p.scale_log2;
-    if ((n0 + BN > Sk) || (causal && n0 + BN - 1 > mw0)) {
+    if (kr.hi(mw0) < n0 + BN - 1 || kr.lo(mw0 + 31) > n0) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        const int lim = (causal ? min(Sk, m + 1) : Sk) - n0 - 32 * nb - 4 * hl;
+        const int base = n0 + 32 * nb + 4 * hl;
+        const int a = kr.lo(m) - base, z = kr.hi(m) - base;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int off = 8 * (r >> 2) + (r & 3);
-          St[nb][r] = off < lim ? St[nb][r] * c2 : -__builtin_inff();
+          St[nb][r] = (off >= a && off <= z) ? St[nb][r] * c2 : -__builtin_inff();
         }
       }
     } else {
@@ -192,17 +197,18 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(const FwdParams p) {
       }
   };
 
-  for (int j = 0; j < j_end; ++j) {
+  for (int j = j_begin; j < j_end; ++j) {
     step_body(smem + (j & 1) * C::BUF, smem + ((j + 1) & 1) * C::BUF, j);
     wait_vm_all();  // the next tile has landed
     barrier_lds();  // and nobody reads this one any more before it is overwritten
   }
 
   // ---- epilogue: O = O^T / rowsum, written row by row (register r of block db holds
-  // column 32 db + 8 (r / 4) + 4 hl + r % 4 of this lane's row); LSE in natural log.
+  // column 32 db + 8 (r / 4) + 4 hl + r % 4 of this lane's row); LSE in natural log.  A row
+  // that may attend no key (possible with a window) gets O = 0 and LSE = log 0 = -inf.
   const float ltot = lsum + __shfl_xor(lsum, 32);
   if (m < Sq) {
-    const float inv = 1.f / ltot;
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     T* Og = (T*)p.o + (q_off + m) * HD;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)

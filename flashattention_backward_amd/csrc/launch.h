@@ -31,6 +31,7 @@ struct FwdParams {
   float* lse;
   int B, H, H_kv, Sq, Sk;
   int causal;
+  int win;           // sliding window in keys, 0 = none (see KeyRange in common.h)
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
   int n_units;       // B * H_kv
@@ -48,6 +49,7 @@ struct BwdParams {
   void* dv;
   int B, H, H_kv, Sq, Sk, Sq_pad;
   int causal;
+  int win;            // sliding window in keys, 0 = none (see KeyRange in common.h)
   float scale;
   float scale_log2;  // scale * log2(e), never zero or subnormal
   float mask_s;      // a score replaced by mask_s gets exponent mask_s * scale_log2 = -inf

@@ -48,7 +48,10 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const PreParams p) {
 #pragma unroll
     for (int w = L / 2; w > 0; w >>= 1) acc += __shfl_xor(acc, w, L);
     if (sub == 0 && row < rows) {
-      const float l2 = valid ? p.lse[src_row] * kLog2e : __builtin_inff();
+      // A row with LSE = -inf may attend no key (a window can leave a row without keys); it
+      // gets the padding rows' +inf, so that exp2(score - lse2) is 0 on all its pairs.
+      const float lse = valid ? p.lse[src_row] : -__builtin_inff();
+      const float l2 = lse == -__builtin_inff() ? __builtin_inff() : lse * kLog2e;
       *reinterpret_cast<float2*>(p.stats + 2 * row) = make_float2(l2, valid ? acc : 0.f);
     }
   }

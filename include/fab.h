@@ -23,6 +23,14 @@
  * Grouped-query heads: H % H_kv == 0 and query head h uses kv head h / (H / H_kv)
  * (contiguous groups); dK and dV are the sums over the H / H_kv query heads of a group.
  * Causal masking is top-left aligned: query row i may attend key j iff j <= i.
+ * Sliding window (`window_size`, the argument autograd_attention.rs passes to both the
+ * forward and the backward, and which flash_bwd.rs's backward rejects unless it is 0):
+ * window_size = W > 0 keeps W keys per query: row i may attend key j only if j > i - W and,
+ * without the causal mask, also j < i + W (same top-left indices as the causal mask).  W = 0
+ * means no window; a window of at least max(Sq, Sk) keys cuts nothing.  Negative W is
+ * FAB_ERR_INVALID_ARGUMENT.  A row left with no key (possible only with a window and
+ * Sq - Sk >= W) gets o = 0 and lse = -inf from fab_fwd, and dq = 0 from fab_bwd; it adds
+ * nothing to dk and dv.
  * Supported: dtype FAB_F32 / FAB_F16 / FAB_BF16 (one dtype shared by all element-typed
  * tensors of a call), head dim D in {64, 128}.
  *
@@ -66,7 +74,8 @@ const char* fab_last_error(void);
  * Layout, as written by the preprocessing step: float32 pairs
  *   ws[((b * H + h) * Sq_pad + i) * 2 + 0] = lse[b, h, i] * log2(e)
  *   ws[((b * H + h) * Sq_pad + i) * 2 + 1] = D[b, h, i] = sum_d dO[b,h,i,d] * o[b,h,i,d]
- * with Sq_pad = Sq rounded up to a multiple of 64; rows i >= Sq hold {+inf, 0}.  fab_bwd
+ * with Sq_pad = Sq rounded up to a multiple of 64; rows i >= Sq, and rows whose lse is -inf
+ * (rows with no allowed key), hold +inf in place of lse * log2(e).  fab_bwd
  * overwrites the workspace on every call; its contents on entry do not matter.
  */
 size_t fab_bwd_workspace_bytes(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype);
@@ -76,11 +85,12 @@ size_t fab_bwd_workspace_bytes(int B, int H, int H_kv, int Sq, int Sk, int D, in
  * returns the output and the lse that the backward consumes):
  *   o   = softmax(scale * q k^T over the allowed keys) v        [B, H, Sq, D], dtype
  *   lse = natural-log log-sum-exp of the allowed scaled scores  [B, H, Sq],   float32
- * q, k, v, o, lse: device pointers, 16-byte aligned, not overlapping o/lse.
+ * q, k, v, o, lse: device pointers, 16-byte aligned, not overlapping o/lse.  The allowed
+ * keys of a row follow `causal` and `window_size` as described at the top of this file.
  */
 fab_status fab_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int H_kv, int Sq, int Sk, int D, int dtype,
-                   int causal, float scale, void* stream);
+                   int causal, int window_size, float scale, void* stream);
 
 /*
  * Step 1 of the backward on its own (flash_bwd.rs, "Step 1: Preprocessing"):
@@ -97,15 +107,15 @@ fab_status fab_bwd_preprocess(const void* dO, const void* o, const float* lse,
 /*
  * Backward (flash_bwd.rs, flash_attention_bwd_impl; autograd_attention.rs,
  * FlashAttentionBackward::backward):
- *   P  = exp(scale * q k^T - lse) on allowed pairs, 0 elsewhere
+ *   P  = exp(scale * q k^T - lse) on allowed pairs (causal, window_size), 0 elsewhere
  *   dP = dO v^T,   dS = P * (dP - D) with D = rowsum(dO * o)
  *   dV = sum over the group's query heads of P^T dO
  *   dK = scale * sum over the group's query heads of dS^T q
  *   dQ = scale * dS k
  * Inputs dO, q, o: [B, num_heads, Sq, D]; k, v: [B, num_kv_heads, Sk, D]; lse as produced
  * by fab_fwd.  Outputs dq [B, num_heads, Sq, D], dk and dv [B, num_kv_heads, Sk, D], all in
- * `dtype`; they need no initialisation and every element is written (rows a causal mask
- * never reaches get 0).  workspace: at least fab_bwd_workspace_bytes(...) bytes of device
+ * `dtype`; they need no initialisation and every element is written (rows the mask never
+ * reaches get 0).  workspace: at least fab_bwd_workspace_bytes(...) bytes of device
  * memory.  All pointers 16-byte aligned; outputs must not overlap inputs or each other.
  * Deterministic: no atomics, identical inputs give bitwise identical outputs.
  */
@@ -113,7 +123,7 @@ fab_status fab_bwd(const void* dO, const void* q, const void* k, const void* v,
                    const void* o, const float* lse, void* dq, void* dk, void* dv,
                    void* workspace, size_t workspace_bytes,
                    int B, int num_heads, int num_kv_heads, int Sq, int Sk, int D, int dtype,
-                   int causal, float scale, void* stream);
+                   int causal, int window_size, float scale, void* stream);
 
 /*
  * The two kernels of step 2 on their own, for inspection and per-kernel timing; fab_bwd
@@ -126,11 +136,11 @@ fab_status fab_bwd(const void* dO, const void* q, const void* k, const void* v,
 fab_status fab_bwd_dkdv(const void* dO, const void* q, const void* k, const void* v,
                         const void* workspace, size_t workspace_bytes, void* dk, void* dv,
                         int B, int num_heads, int num_kv_heads, int Sq, int Sk, int D,
-                        int dtype, int causal, float scale, void* stream);
+                        int dtype, int causal, int window_size, float scale, void* stream);
 fab_status fab_bwd_dq(const void* dO, const void* q, const void* k, const void* v,
                       const void* workspace, size_t workspace_bytes, void* dq,
                       int B, int num_heads, int num_kv_heads, int Sq, int Sk, int D,
-                      int dtype, int causal, float scale, void* stream);
+                      int dtype, int causal, int window_size, float scale, void* stream);
 
 #ifdef __cplusplus
 }

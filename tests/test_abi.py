@@ -42,12 +42,12 @@ P = 1 << 20  # a fake, 16-byte aligned address: validation must fail before usin
 
 def bwd(**kw):
     a = dict(dO=P, q=P, k=P, v=P, o=P, lse=P, dq=P, dk=P, dv=P, ws=P, ws_bytes=1 << 40,
-             B=1, H=4, H_kv=2, Sq=16, Sk=16, D=64, dtype=2, causal=1, scale=0.125)
+             B=1, H=4, H_kv=2, Sq=16, Sk=16, D=64, dtype=2, causal=1, window=0, scale=0.125)
     a.update(kw)
     L = fab.lib()
     st = L.fab_bwd(a["dO"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["dq"], a["dk"], a["dv"],
                    a["ws"], a["ws_bytes"], a["B"], a["H"], a["H_kv"], a["Sq"], a["Sk"], a["D"],
-                   a["dtype"], a["causal"], a["scale"], None)
+                   a["dtype"], a["causal"], a["window"], a["scale"], None)
     return st, L.fab_last_error().decode()
 
 
@@ -66,6 +66,7 @@ def bwd(**kw):
     (dict(ws_bytes=10), 1, "workspace"),
     (dict(scale=float("inf")), 1, "scale"),
     (dict(scale=float("nan")), 1, "scale"),
+    (dict(window=-1), 1, "window_size"),
     (dict(B=4096, Sq=65536, D=128, H=8, H_kv=8), 1, "2^31"),
 ])
 def test_bwd_rejects_invalid_arguments(kw, status, needle):
@@ -76,19 +77,23 @@ def test_bwd_rejects_invalid_arguments(kw, status, needle):
 
 def test_fwd_and_preprocess_reject_invalid_arguments():
     L = fab.lib()
-    st = L.fab_fwd(P, P, 0, P, P, 1, 2, 1, 8, 8, 64, 1, 0, 0.1, None)
+    st = L.fab_fwd(P, P, 0, P, P, 1, 2, 1, 8, 8, 64, 1, 0, 0, 0.1, None)
     assert st == 1 and "v: null" in L.fab_last_error().decode()
-    st = L.fab_fwd(P, P, P, P, P, 1, 2, 1, 8, 8, 64, 1, 0, float("nan"), None)
+    st = L.fab_fwd(P, P, P, P, P, 1, 2, 1, 8, 8, 64, 1, 0, 0, float("nan"), None)
     assert st == 1 and "scale" in L.fab_last_error().decode()
+    st = L.fab_fwd(P, P, P, P, P, 1, 2, 1, 8, 8, 64, 1, 1, -3, 0.1, None)
+    assert st == 1 and "window_size" in L.fab_last_error().decode()
     st = L.fab_bwd_preprocess(P, P, P + 2, P, 1 << 30, 1, 2, 8, 128, 0, None)
     assert st == 1 and "lse" in L.fab_last_error().decode()
     st = L.fab_bwd_preprocess(P, P, P, P, 16, 1, 2, 8, 128, 0, None)
     assert st == 1 and "workspace" in L.fab_last_error().decode()
     st = L.fab_bwd_preprocess(P, P, P, P, 1 << 30, 1, 2, 8, 32, 0, None)
     assert st == 2
-    st = L.fab_bwd_dkdv(P, P, P, P, P, 1 << 30, P, 0, 1, 2, 1, 8, 8, 64, 2, 1, 0.1, None)
+    st = L.fab_bwd_dkdv(P, P, P, P, P, 1 << 30, P, 0, 1, 2, 1, 8, 8, 64, 2, 1, 0, 0.1, None)
     assert st == 1 and "dv: null" in L.fab_last_error().decode()
-    st = L.fab_bwd_dq(P, P, P, P, P, 8, P, 1, 2, 1, 8, 8, 64, 2, 1, 0.1, None)
+    st = L.fab_bwd_dkdv(P, P, P, P, P, 1 << 30, P, P, 1, 2, 1, 8, 8, 64, 2, 1, -1, 0.1, None)
+    assert st == 1 and "window_size" in L.fab_last_error().decode()
+    st = L.fab_bwd_dq(P, P, P, P, P, 8, P, 1, 2, 1, 8, 8, 64, 2, 1, 0, 0.1, None)
     assert st == 1 and "workspace" in L.fab_last_error().decode()
 
 

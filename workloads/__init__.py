@@ -33,6 +33,7 @@ class Workload:
     causal: bool
     seed: int
     do_std: float = 1.0
+    window: int = 0     # sliding window in keys (0 = none)
 
     @property
     def scale(self) -> float:
@@ -42,11 +43,23 @@ class Workload:
     def group(self) -> int:
         return self.H // self.H_kv
 
+    def allowed_pairs(self) -> float:
+        """(b, h, query, key) pairs counted as work: B*H*Sq*Sk, halved when causal (the fixed
+        half of the metric, not the exact (S+1)/2S); with a window, the exact number of
+        pairs it keeps (query i keeps keys j with i - W < j <= i, or |i - j| < W without
+        the causal mask, below Sk)."""
+        if self.window <= 0:
+            p = float(self.B) * self.H * self.Sq * self.Sk
+            return p / 2 if self.causal else p
+        i = np.arange(self.Sq, dtype=np.int64)
+        lo = np.maximum(i - self.window + 1, 0)
+        hi = np.minimum(i if self.causal else i + self.window - 1, self.Sk - 1)
+        return float(self.B) * self.H * float(np.maximum(hi - lo + 1, 0).sum())
+
     def bwd_flops(self) -> float:
-        """Counted backward FLOPs: 10*B*H*Sq*Sk*D, halved when causal (the five
-        contractions over the pairs the method must visit)."""
-        f = 10.0 * self.B * self.H * self.Sq * self.Sk * self.D
-        return f / 2 if self.causal else f
+        """Counted backward FLOPs: 10*D per allowed pair (the five contractions over the
+        pairs the method must visit)."""
+        return 10.0 * self.D * self.allowed_pairs()
 
     def describe(self) -> dict:
         d = dataclasses.asdict(self)
@@ -62,6 +75,9 @@ WORKLOADS = {w.name: w for w in [
     Workload("bf16_gqa4_causal_h32_s4096_d128", "bf16", 2, 32, 8, 4096, 4096, 128, True, seed=4),
     Workload("fp16_causal_h16_s16384_d128", "fp16", 1, 16, 16, 16384, 16384, 128, True, seed=51),
     Workload("fp16_gqa4_h16_sq512_sk8192_d128", "fp16", 4, 16, 4, 512, 8192, 128, False, seed=52),
+    # sliding window of 4096 keys over 16384 positions (a long-context local-attention shape)
+    Workload("bf16_gqa4_causal_win4096_h16_s16384_d128", "bf16", 1, 16, 4, 16384, 16384, 128, True,
+             seed=6, window=4096),
 ]}
 
 # The grouped-query causal bf16 case at S=4096, D=128 is the throughput headline.
