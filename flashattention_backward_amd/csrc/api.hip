@@ -54,14 +54,19 @@ constexpr long long kMaxElems = (1LL << 31) - 1;
 
 size_t elem_size(int dt) { return dt == FAB_F32 ? 4 : 2; }
 
+// bf16 / fp16 at head dims 32 to 128 run the tiled kernels (fwd16.hip, bwd16.hip); fp32, and
+// bf16 / fp16 at head dim 256, run the generic ones (fwd.hip, bwd_dkdv.hip, bwd_dq.hip).
+bool tiled(int dtype, int D) { return dtype != FAB_F32 && D <= 128; }
+
 fab_status check_common(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype) {
   if (dtype != FAB_F32 && dtype != FAB_F16 && dtype != FAB_BF16)
     return fail(FAB_ERR_UNSUPPORTED, "dtype", "unsupported dtype code %d (expected 0=f32, 1=f16, 2=bf16)", dtype);
   if (B < 1 || H < 1 || H_kv < 1 || Sq < 1 || Sk < 1 || D < 1)
     return fail(FAB_ERR_INVALID_ARGUMENT, "dims",
                 "every size must be >= 1 (B=%d H=%d H_kv=%d Sq=%d Sk=%d D=%d)", B, H, H_kv, Sq, Sk, D);
-  if (D != 64 && D != 128)
-    return fail(FAB_ERR_UNSUPPORTED, "head_dim", "head dim %d not supported (64 or 128)", D);
+  if (D != 32 && D != 64 && D != 96 && D != 128 && !(D == 256 && dtype != FAB_F32))
+    return fail(FAB_ERR_UNSUPPORTED, "head_dim",
+                "head dim %d not supported (32, 64, 96, 128; also 256 for f16/bf16)", D);
   if (H % H_kv != 0)
     return fail(FAB_ERR_INVALID_ARGUMENT, "num_kv_heads",
                 "num_heads %d is not a multiple of num_kv_heads %d", H, H_kv);
@@ -198,12 +203,12 @@ hipError_t launch_step2(const fab::BwdParams& p, int dtype, int D, hipStream_t s
                         fab::LaunchInfo* li) {
   hipError_t e = hipSuccess;
   if (dkdv) {
-    e = dtype == FAB_F32 ? fab::launch_bwd_dkdv(p, dtype, D, s, li) : fab::launch_bwd_dkdv16(p, dtype, D, s, li);
+    e = tiled(dtype, D) ? fab::launch_bwd_dkdv16(p, dtype, D, s, li) : fab::launch_bwd_dkdv(p, dtype, D, s, li);
     if (e != hipSuccess) return e;
     log_launch(*li);
   }
   if (dq) {
-    e = dtype == FAB_F32 ? fab::launch_bwd_dq(p, dtype, D, s, li) : fab::launch_bwd_dq16(p, dtype, D, s, li);
+    e = tiled(dtype, D) ? fab::launch_bwd_dq16(p, dtype, D, s, li) : fab::launch_bwd_dq(p, dtype, D, s, li);
     if (e != hipSuccess) return e;
     log_launch(*li);
   }
@@ -260,8 +265,8 @@ fab_status fab_fwd(const void* q, const void* k, const void* v, void* o, float* 
   p.n_units = B * H_kv;
   p.units_per_xcd = units_per_xcd(p.n_units);
   fab::LaunchInfo li;
-  const hipError_t e = dtype == FAB_F32 ? fab::launch_fwd(p, dtype, D, (hipStream_t)stream, &li)
-                                        : fab::launch_fwd16(p, dtype, D, (hipStream_t)stream, &li);
+  const hipError_t e = tiled(dtype, D) ? fab::launch_fwd16(p, dtype, D, (hipStream_t)stream, &li)
+                                       : fab::launch_fwd(p, dtype, D, (hipStream_t)stream, &li);
   FAB_TRY(launched(e, "fwd"));
   log_launch(li);
   return FAB_OK;

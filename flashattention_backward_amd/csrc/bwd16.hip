@@ -56,6 +56,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   typedef typename Frag<T>::type F;
   typedef TileDma<T, HD, Dkdv16<HD>::BM> Dma;
   constexpr int NC = HD / 16, NDB = HD / 32;
+  static_assert(C::KMAX <= NC, "a tile's prefetch is spread over the head-dim slices");
   constexpr int BM = C::BM, BN = C::BN;
   typedef typename C::L L;
   constexpr unsigned ROWB = HD * sizeof(T);
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
     // holds registers 8 ks .. 8 ks + 7 of block nb.  The dP MFMAs are volatile asm and every
     // exponential is pinned between them with order_point(), so the interleave is exact.
     F pa[2][2], da[2][2];
-    constexpr int PER_CC = 32 / NC;  // exponentials per head-dim slice
+    constexpr int PER_CC = (32 + NC - 1) / NC;  // exponentials per head-dim slice
     auto pexp = [&](int e) {
       const int nb = e >> 4, r = e & 15;
       float x = fast_exp2(S[nb][r] * p.scale_log2 - l2[r]);
@@ -287,11 +288,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
       if (cc == 0) mma_v0(dP[0], ad[cc], bv0[cc]);
       else mma_v(dP[0], ad[cc], bv0[cc]);
 #pragma unroll
-      for (int k = 0; k < PER_CC / 2; ++k) pexp(cc * PER_CC + k);
+      for (int k = 0; k < PER_CC / 2; ++k)
+        if (cc * PER_CC + k < 32) pexp(cc * PER_CC + k);
       if (cc == 0) mma_v0(dP[1], ad[cc], bv1[cc]);
       else mma_v(dP[1], ad[cc], bv1[cc]);
 #pragma unroll
-      for (int k = PER_CC / 2; k < PER_CC; ++k) pexp(cc * PER_CC + k);
+      for (int k = PER_CC / 2; k < PER_CC; ++k)
+        if (cc * PER_CC + k < 32) pexp(cc * PER_CC + k);
     }
     mma_vdrain(dP);
     __builtin_amdgcn_sched_barrier(0);
@@ -312,7 +315,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
     F bo[NDB], bq[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) bo[db] = b_do(db, 0);
-    constexpr int PER_MMA = 16 / (2 * NDB);  // dS elements per MFMA of a 16-row slice
+    constexpr int PER_MMA = (16 + 2 * NDB - 1) / (2 * NDB);  // dS elements per MFMA of a 16-row slice
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       bq[db] = b_q(db, 0);
@@ -323,7 +326,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
 #pragma unroll
         for (int k = 0; k < PER_MMA; ++k) {
           const int e = (2 * db + nb) * PER_MMA + k;  // 0..15 over rows 0..15 of both blocks
-          ds(e & 1, e >> 1);
+          if (e < 16) ds(e & 1, e >> 1);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -339,7 +342,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
 #pragma unroll
         for (int k = 0; k < PER_MMA; ++k) {
           const int e = (2 * db + nb) * PER_MMA + k;
-          ds(e & 1, 8 + (e >> 1));
+          if (e < 16) ds(e & 1, 8 + (e >> 1));
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -465,6 +468,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(const BwdParams p) {
   typedef Dq16<HD, NB> C;
   typedef typename Frag<T>::type F;
   constexpr int NC = HD / 16, NDB = HD / 32;
+  static_assert(C::KMAX <= NC, "a tile's prefetch is spread over the head-dim slices");
   constexpr int BM = C::BM, BN = C::BN, STAGES = C::STAGES;
   typedef typename C::L L;
 
@@ -603,7 +607,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(const BwdParams p) {
     // is formed while the current slice's MFMAs run.
 #pragma unroll
     for (int r = 0; r < 8; ++r) elem(0, r);
-    constexpr int PER = 8 / NDB;  // next-slice elements per MFMA
+    constexpr int PER = (8 + NDB - 1) / NDB;  // next-slice elements per MFMA
 #pragma unroll
     for (int sl = 0; sl < 2 * NB; ++sl) {
       const int nb = sl >> 1, ks = sl & 1;
@@ -616,7 +620,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(const BwdParams p) {
         mma_a(dq[db], da[nb][ks], bk);
         if (sl + 1 < 2 * NB) {
 #pragma unroll
-          for (int k = 0; k < PER; ++k) elem((sl + 1) >> 1, 8 * ((sl + 1) & 1) + db * PER + k);
+          for (int k = 0; k < PER; ++k)
+            if (db * PER + k < 8) elem((sl + 1) >> 1, 8 * ((sl + 1) & 1) + db * PER + k);
         }
         if (db + 1 < NDB) bk = bk_n;
         __builtin_amdgcn_sched_barrier(0);
@@ -673,14 +678,32 @@ static hipError_t go_dq(const BwdParams& p, hipStream_t s, LaunchInfo* info) {
   return hipGetLastError();
 }
 
+template <class T>
+static hipError_t dkdv_hd(const BwdParams& p, int hd, hipStream_t s, LaunchInfo* info) {
+  switch (hd) {
+    case 32: return go_dkdv<T, 32>(p, s, info);
+    case 64: return go_dkdv<T, 64>(p, s, info);
+    case 96: return go_dkdv<T, 96>(p, s, info);
+    default: return go_dkdv<T, 128>(p, s, info);
+  }
+}
+
+template <class T>
+static hipError_t dq_hd(const BwdParams& p, int hd, hipStream_t s, LaunchInfo* info) {
+  switch (hd) {
+    case 32: return go_dq<T, 32>(p, s, info);
+    case 64: return go_dq<T, 64>(p, s, info);
+    case 96: return go_dq<T, 96>(p, s, info);
+    default: return go_dq<T, 128>(p, s, info);
+  }
+}
+
 hipError_t launch_bwd_dkdv16(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info) {
-  if (dt == kBF16) return hd == 64 ? go_dkdv<bf16, 64>(p, s, info) : go_dkdv<bf16, 128>(p, s, info);
-  return hd == 64 ? go_dkdv<f16, 64>(p, s, info) : go_dkdv<f16, 128>(p, s, info);
+  return dt == kBF16 ? dkdv_hd<bf16>(p, hd, s, info) : dkdv_hd<f16>(p, hd, s, info);
 }
 
 hipError_t launch_bwd_dq16(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info) {
-  if (dt == kBF16) return hd == 64 ? go_dq<bf16, 64>(p, s, info) : go_dq<bf16, 128>(p, s, info);
-  return hd == 64 ? go_dq<f16, 64>(p, s, info) : go_dq<f16, 128>(p, s, info);
+  return dt == kBF16 ? dq_hd<bf16>(p, hd, s, info) : dq_hd<f16>(p, hd, s, info);
 }
 
 }  // namespace fab

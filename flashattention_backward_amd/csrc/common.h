@@ -76,6 +76,12 @@ __device__ __forceinline__ void mma_drain(f32x16 (&a)[4]) {
 __device__ __forceinline__ void mma_drain(f32x16 (&a)[2]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(a[0]), "+a"(a[1]));
 }
+__device__ __forceinline__ void mma_drain(f32x16 (&a)[3]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]));
+}
+__device__ __forceinline__ void mma_drain(f32x16 (&a)[1]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(a[0]));
+}
 // The same with the accumulator in VGPRs, as volatile asm: the statements keep their order
 // relative to each other and to order_point(), which lets a loop state exactly where vector
 // work goes between MFMAs.  mma_v0 starts a contraction (accumulator input 0); its output
@@ -226,6 +232,26 @@ struct TileLayout<64> {
   __device__ static __forceinline__ void granule(int gi, int& r, int& c) {
     r = gi >> 3;
     c = (gi & 7) ^ swz64(r);
+  }
+};
+
+// Head dims 96 and 32 keep the geometry of 128 and 64: a row uses the first 12 (4) of the
+// 16 (8) chunks its slot has room for, so every read is one the wider layout makes without
+// bank conflicts.  The granules past a row's data load repeats of its first chunks (the
+// copy fills whole tile images), which nothing reads.
+template <>
+struct TileLayout<96> : TileLayout<128> {
+  __device__ static __forceinline__ void granule(int gi, int& r, int& c) {
+    TileLayout<128>::granule(gi, r, c);
+    if (c >= 12) c -= 12;
+  }
+};
+
+template <>
+struct TileLayout<32> : TileLayout<64> {
+  __device__ static __forceinline__ void granule(int gi, int& r, int& c) {
+    TileLayout<64>::granule(gi, r, c);
+    if (c >= 4) c -= 4;
   }
 };
 

@@ -40,6 +40,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(const FwdParams p) {
   typedef typename C::L L;
   typedef typename Frag<T>::type F;
   constexpr int NC = HD / 16, NDB = HD / 32;
+  static_assert(C::KMAX <= NC, "a tile's prefetch is spread over the head-dim slices");
   constexpr int BM = C::BM, BN = C::BN;
   constexpr float kLazy = 8.f;  // log2 growth of a row maximum tolerated without rescaling
 
@@ -234,9 +235,18 @@ static hipError_t go16(const FwdParams& p, hipStream_t s, LaunchInfo* info) {
   return hipGetLastError();
 }
 
+template <class T>
+static hipError_t fwd_hd(const FwdParams& p, int hd, hipStream_t s, LaunchInfo* info) {
+  switch (hd) {
+    case 32: return go16<T, 32>(p, s, info);
+    case 64: return go16<T, 64>(p, s, info);
+    case 96: return go16<T, 96>(p, s, info);
+    default: return go16<T, 128>(p, s, info);
+  }
+}
+
 hipError_t launch_fwd16(const FwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info) {
-  if (dt == kBF16) return hd == 64 ? go16<bf16, 64>(p, s, info) : go16<bf16, 128>(p, s, info);
-  return hd == 64 ? go16<f16, 64>(p, s, info) : go16<f16, 128>(p, s, info);
+  return dt == kBF16 ? fwd_hd<bf16>(p, hd, s, info) : fwd_hd<f16>(p, hd, s, info);
 }
 
 }  // namespace fab

@@ -11,10 +11,19 @@
 
 namespace fab {
 
+// Lanes that share a row: its number of 16-byte chunks rounded up to a power of two, at most
+// 64 (a lane sums chunks sub, sub + L, ...; lanes past the last chunk idle).
+constexpr int lanes_per_row(int chunks) {
+  int l = 1;
+  while (l < chunks && l < 64) l *= 2;
+  return l;
+}
+
 template <class T, int HD>
 __global__ __launch_bounds__(256) void preprocess_kernel(const PreParams p) {
   constexpr int E = 16 / sizeof(T);          // elements per 16-byte load
-  constexpr int L = HD / E;                  // lanes per row (power of two, <= 64)
+  constexpr int CH = HD / E;                 // 16-byte chunks per row
+  constexpr int L = lanes_per_row(CH);
   constexpr int ROWS_PER_PASS = 256 / L;
   constexpr int PASSES = 4;
   const int tid = threadIdx.x;
@@ -30,8 +39,10 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const PreParams p) {
     const bool valid = row < rows && m < p.Sq;
     const long long src_row = (long long)bh * p.Sq + m;
     float acc = 0.f;
-    if (valid) {
-      const size_t off = (size_t)src_row * HD + sub * E;
+#pragma unroll
+    for (int c = sub; c < CH; c += L) {
+      if (!valid) continue;
+      const size_t off = (size_t)src_row * HD + c * E;
       if constexpr (sizeof(T) == 2) {
         typedef T v8 __attribute__((ext_vector_type(8)));
         const v8 a = *reinterpret_cast<const v8*>(dO + off);
@@ -59,7 +70,7 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const PreParams p) {
 
 template <class T, int HD>
 static hipError_t go(const PreParams& p, hipStream_t s, LaunchInfo* info) {
-  constexpr int rows_per_block = (256 / (HD / (16 / sizeof(T)))) * 4;
+  constexpr int rows_per_block = (256 / lanes_per_row(HD / (16 / sizeof(T)))) * 4;
   const long long rows = (long long)p.BH * p.Sq_pad;
   const long long grid = (rows + rows_per_block - 1) / rows_per_block;
   if (info) *info = LaunchInfo{"preprocess", (int)grid, 256, 0};
@@ -67,10 +78,21 @@ static hipError_t go(const PreParams& p, hipStream_t s, LaunchInfo* info) {
   return hipGetLastError();
 }
 
+template <class T>
+static hipError_t go_hd(const PreParams& p, int hd, hipStream_t s, LaunchInfo* info) {
+  switch (hd) {
+    case 32: return go<T, 32>(p, s, info);
+    case 64: return go<T, 64>(p, s, info);
+    case 96: return go<T, 96>(p, s, info);
+    case 128: return go<T, 128>(p, s, info);
+    default: return go<T, 256>(p, s, info);
+  }
+}
+
 hipError_t launch_preprocess(const PreParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info) {
-  if (dt == kBF16) return hd == 64 ? go<bf16, 64>(p, s, info) : go<bf16, 128>(p, s, info);
-  if (dt == kF16) return hd == 64 ? go<f16, 64>(p, s, info) : go<f16, 128>(p, s, info);
-  return hd == 64 ? go<float, 64>(p, s, info) : go<float, 128>(p, s, info);
+  if (dt == kBF16) return go_hd<bf16>(p, hd, s, info);
+  if (dt == kF16) return go_hd<f16>(p, hd, s, info);
+  return go_hd<float>(p, hd, s, info);
 }
 
 }  // namespace fab

@@ -32,7 +32,8 @@
  * Sq - Sk >= W) gets o = 0 and lse = -inf from fab_fwd, and dq = 0 from fab_bwd; it adds
  * nothing to dk and dv.
  * Supported: dtype FAB_F32 / FAB_F16 / FAB_BF16 (one dtype shared by all element-typed
- * tensors of a call), head dim D in {64, 128}.
+ * tensors of a call); head dim D in {32, 64, 96, 128}, and also 256 for FAB_F16 / FAB_BF16
+ * (kernels are compiled per head dim, as flash_bwd.rs's kernel names carry the head dim).
  *
  * Streams: all work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  * the call returns without waiting.  Results are valid for later work on the same stream.

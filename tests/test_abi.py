@@ -33,7 +33,10 @@ def test_workspace_bytes():
     assert L.fab_bwd_workspace_bytes(1, 1, 1, 3, 5, 64, 0) == 512
     assert L.fab_bwd_workspace_bytes(1, 3, 3, 65, 5, 64, 0) == 3 * 128 * 8
     assert L.fab_bwd_workspace_bytes(1, 3, 2, 3, 5, 64, 0) == 0    # H % H_kv != 0
-    assert L.fab_bwd_workspace_bytes(1, 1, 1, 3, 5, 96, 0) == 0    # head dim
+    assert L.fab_bwd_workspace_bytes(1, 1, 1, 3, 5, 80, 0) == 0    # head dim
+    assert L.fab_bwd_workspace_bytes(1, 1, 1, 3, 5, 256, 0) == 0   # head dim 256 in fp32
+    assert L.fab_bwd_workspace_bytes(1, 1, 1, 3, 5, 256, 2) > 0    # ... but not in bf16
+    assert L.fab_bwd_workspace_bytes(1, 1, 1, 3, 5, 96, 1) > 0
     assert L.fab_bwd_workspace_bytes(1, 1, 1, 3, 5, 64, 9) == 0    # dtype
 
 
@@ -53,7 +56,8 @@ def bwd(**kw):
 
 @pytest.mark.parametrize("kw,status,needle", [
     (dict(dtype=3), 2, "dtype"),
-    (dict(D=96), 2, "head_dim"),
+    (dict(D=80), 2, "head_dim"),
+    (dict(D=256, dtype=0), 2, "head_dim"),
     (dict(D=0), 1, "dims"),
     (dict(B=0), 1, "dims"),
     (dict(Sq=0), 1, "dims"),
@@ -87,7 +91,7 @@ def test_fwd_and_preprocess_reject_invalid_arguments():
     assert st == 1 and "lse" in L.fab_last_error().decode()
     st = L.fab_bwd_preprocess(P, P, P, P, 16, 1, 2, 8, 128, 0, None)
     assert st == 1 and "workspace" in L.fab_last_error().decode()
-    st = L.fab_bwd_preprocess(P, P, P, P, 1 << 30, 1, 2, 8, 32, 0, None)
+    st = L.fab_bwd_preprocess(P, P, P, P, 1 << 30, 1, 2, 8, 48, 0, None)
     assert st == 2
     st = L.fab_bwd_dkdv(P, P, P, P, P, 1 << 30, P, 0, 1, 2, 1, 8, 8, 64, 2, 1, 0, 0.1, None)
     assert st == 1 and "dv: null" in L.fab_last_error().decode()
