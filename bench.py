@@ -19,6 +19,7 @@ sample of the same workload, timed on this host's cores before the GPU is touche
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
        python bench.py --only {bwd,dkdv,dq,preprocess,fwd,copy}   (a launch loop for rocprofv3)
+       python bench.py --atomics   (fp32 atomic-add bandwidth probe)
 """
 from __future__ import annotations
 
@@ -315,6 +316,41 @@ def only_mode(w, what, steps, warmup):
     print(json.dumps({"only": what, "workload": w.name, "launches": warmup + steps}), flush=True)
 
 
+def atomics_probe(steps, warmup):
+    """fp32 atomic-add bandwidth against plain stores and read-modify-writes, in 32 KiB tiles
+    (one 64 x 128 fp32 block of a dQ accumulator), from the kernels of libfab_probe.so; and
+    what the atomic dQ route of the headline workload would cost at the measured rate."""
+    import torch
+    from flashattention_backward_amd import build as fab_build
+    if not os.path.exists(fab_build.PROBE_LIB):
+        raise RuntimeError(f"{fab_build.PROBE_LIB} is missing: build first")
+    L = ctypes.CDLL(fab_build.PROBE_LIB)
+    L.fab_probe_launch.restype = ctypes.c_int
+    L.fab_probe_launch.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 4 + [ctypes.c_void_p]
+    ntiles, blocks, iters, tile = 4096, 1024, 32, 32768   # a 128 MiB buffer
+    buf = torch.zeros(ntiles * tile // 4, dtype=torch.float32, device="cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    payload = blocks * iters * tile
+    names = ["atomic_add_scattered", "atomic_add_xcd_local", "plain_store", "plain_rmw"]
+    res = {}
+    for mode, name in enumerate(names):
+        def launch():
+            if L.fab_probe_launch(buf.data_ptr(), ntiles, blocks, iters, mode, stream) != 0:
+                raise RuntimeError("probe launch failed")
+        ms = time_launches(launch, steps, warmup)
+        res[name] = {"ms": round(ms, 4), "TB_per_s": round(payload / (ms * 1e-3) / 1e12, 3)}
+    w = workloads.get(workloads.HEADLINE)
+    # the atomic route adds one D-wide fp32 row per (key tile of 128, query row it reaches)
+    n_kt = -(-w.Sk // 128)
+    visits = sum(min(n_kt, i // 128 + 1) for i in range(w.Sq)) if w.causal else w.Sq * n_kt
+    atomic_bytes = w.B * w.H * visits * w.D * 4
+    rate = res["atomic_add_scattered"]["TB_per_s"] * 1e12
+    return {"probe": "fp32 atomic add vs plain stores (32 KiB tiles)", "payload_bytes": payload,
+            "blocks": blocks, "iters": iters, "buffer_bytes": ntiles * tile, "results": res,
+            "headline_atomic_dq_bytes": atomic_bytes,
+            "headline_atomic_dq_ms_at_measured_rate": round(atomic_bytes / rate * 1e3, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -324,6 +360,8 @@ def main():
     ap.add_argument("--all", action="store_true", help="one JSON line per named workload (no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["bwd", "dkdv", "dq", "preprocess", "fwd", "copy"])
+    ap.add_argument("--atomics", action="store_true",
+                    help="fp32 atomic-add bandwidth probe (the measurement behind the dQ design)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -331,6 +369,9 @@ def main():
               f"--gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
     w = workloads.get(args.workload)
+    if args.atomics:
+        print(json.dumps(atomics_probe(args.steps, args.warmup)), flush=True)
+        return
     if args.only:
         only_mode(w, args.only, args.steps, args.warmup)
         return

@@ -3,8 +3,9 @@
     python -m flashattention_backward_amd.build        # or __graft_entry__.build()
 
 Each .hip source is compiled to an object under ``_build/`` in parallel, then linked into
-``flashattention_backward_amd/libfab.so``.  Always recompiles (the build check must exercise
-the compiler every time).
+``flashattention_backward_amd/libfab.so``.  The measurement kernels of ``csrc/probe/`` (not part
+of the library) are linked on their own into ``libfab_probe.so``.  Always recompiles (the build
+check must exercise the compiler every time).
 """
 from __future__ import annotations
 
@@ -19,6 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfab.so")
+PROBE_LIB = os.path.join(PKG, "libfab_probe.so")
+PROBE_SOURCES = ["probe/atomic_bandwidth.hip"]
 SOURCES = ["api.hip", "preprocess.hip", "bwd_dkdv.hip", "bwd_dq.hip", "bwd16.hip", "fwd.hip", "fwd16.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -46,7 +49,7 @@ def device_asm_path(src: str) -> str:
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    obj = os.path.join(BUILD, os.path.splitext(src)[0].replace("/", "_") + ".o")
     cmd = [HIPCC, *DEVICE_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", os.path.join(ROOT, "include"),
            "-c", os.path.join(CSRC, src), "-o", obj]
     cwd = None
@@ -68,18 +71,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str):
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"[fab] built {LIB}")
+        print(f"[fab] built {LIB} and {os.path.basename(PROBE_LIB)}")
     return LIB
 
 

@@ -123,3 +123,17 @@ def test_python_binding_rejects_cpu_tensors():
         fab.fwd(q, q, q)
     with pytest.raises(ValueError, match="4-D"):
         fab.bwd(q, q[0], q, q, q, q[..., 0])
+
+
+def test_probe_library_exports_and_validates():
+    """The atomic-bandwidth probe library (bench.py --atomics) loads, exports its launcher and
+    rejects invalid arguments before touching the GPU."""
+    from flashattention_backward_amd import build as fab_build
+    L = ctypes.CDLL(fab_build.PROBE_LIB)
+    f = L.fab_probe_launch
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 4 + [ctypes.c_void_p]
+    assert f(None, 64, 8, 1, 0, None) == 1          # null buffer
+    assert f(P, 12, 8, 1, 0, None) == 1             # tiles not a multiple of 8
+    assert f(P, 64, 8, 1, 4, None) == 1             # no such mode
+    assert f(P, 64, 0, 1, 0, None) == 1             # no workgroups
