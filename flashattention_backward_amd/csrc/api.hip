@@ -142,6 +142,7 @@ fab::BwdParams bwd_params(const void* dO, const void* q, const void* k, const vo
   fab::BwdParams p;
   p.q = q; p.k = k; p.v = v; p.dO = dO; p.stats = static_cast<const float*>(workspace);
   p.dq = dq; p.dk = dk; p.dv = dv;
+  p.o = nullptr; p.lse = nullptr; p.stats_out = nullptr;
   p.B = B; p.H = H; p.H_kv = H_kv; p.Sq = Sq; p.Sk = Sk; p.Sq_pad = fab::stats_rows(Sq);
   p.causal = causal ? 1 : 0;
   p.win = kernel_window(window_size, Sq, Sk);
@@ -316,11 +317,22 @@ fab_status fab_bwd(const void* dO, const void* q, const void* k, const void* v,
 
   hipStream_t s = (hipStream_t)stream;
   fab::LaunchInfo li;
+  const fab::BwdParams p =
+      bwd_params(dO, q, k, v, workspace, dq, dk, dv, B, H, H_kv, Sq, Sk, causal, window_size, scale);
+  if (tiled(dtype, D)) {
+    // Step 1 runs inside the dQ kernel, which therefore goes first: it writes the row
+    // statistics the dK/dV kernel then reads from the workspace.
+    fab::BwdParams pq = p;
+    pq.o = o; pq.lse = lse; pq.stats_out = static_cast<float*>(workspace);
+    FAB_TRY(launched(fab::launch_bwd_dq16(pq, dtype, D, s, &li), "bwd_dq"));
+    log_launch(li);
+    FAB_TRY(launched(fab::launch_bwd_dkdv16(p, dtype, D, s, &li), "bwd_dkdv"));
+    log_launch(li);
+    return FAB_OK;
+  }
   const fab::PreParams pp = pre_params(dO, o, lse, workspace, B, H, Sq);
   FAB_TRY(launched(fab::launch_preprocess(pp, dtype, D, s, &li), "preprocess"));
   log_launch(li);
-  const fab::BwdParams p =
-      bwd_params(dO, q, k, v, workspace, dq, dk, dv, B, H, H_kv, Sq, Sk, causal, window_size, scale);
   FAB_TRY(launched(launch_step2(p, dtype, D, s, true, true, &li), "step 2"));
   return FAB_OK;
 }

@@ -508,9 +508,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(const BwdParams p) {
       qf[cc] = ld8(Qg + (size_t)mc * HD + 16 * cc + 8 * hl);
       dof[cc] = ld8(dOg + (size_t)mc * HD + 16 * cc + 8 * hl);
     }
-    const float* st = p.stats + ((size_t)(b * p.H + hq) * p.Sq_pad + mc) * 2;
-    lse2 = m < Sq ? st[0] : __builtin_inff();
-    dl = m < Sq ? st[1] : 0.f;
+    if (p.stats_out != nullptr) {
+      // Step 1 fused: D = sum_d dO * O of this lane's row, over the two lanes that hold it,
+      // and the row's LSE in base 2 (a row with LSE = -inf attends no key and, like a
+      // padding row, gets +inf).  The dK/dV kernel reads both from stats_out.
+      const T* Og = (const T*)p.o + q_off * HD;
+      float acc = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        const F of = ld8(Og + (size_t)mc * HD + 16 * cc + 8 * hl);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += (float)dof[cc][e] * (float)of[e];
+      }
+      acc += __shfl_xor(acc, 32);
+      const float lse = m < Sq ? p.lse[q_off + m] : -__builtin_inff();
+      lse2 = lse == -__builtin_inff() ? __builtin_inff() : lse * kLog2e;
+      dl = m < Sq ? acc : 0.f;
+      if (hl == 0 && m < p.Sq_pad)
+        *reinterpret_cast<float2*>(p.stats_out + ((size_t)(b * p.H + hq) * p.Sq_pad + m) * 2) =
+            make_float2(lse2, dl);
+    } else {
+      const float* st = p.stats + ((size_t)(b * p.H + hq) * p.Sq_pad + mc) * 2;
+      lse2 = m < Sq ? st[0] : __builtin_inff();
+      dl = m < Sq ? st[1] : 0.f;
+    }
   }
 
   f32x16 dq[NDB];

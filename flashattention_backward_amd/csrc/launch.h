@@ -44,6 +44,12 @@ struct BwdParams {
   const void* v;
   const void* dO;
   const float* stats;  // see PreParams
+  // Set on the dQ kernel of fab_bwd (16-bit path): the kernel forms its rows' statistics
+  // itself from o and lse, as the preprocess would, and writes them to stats_out for the
+  // dK/dV kernel that follows.  Null otherwise (the statistics come from the preprocess).
+  const void* o;
+  const float* lse;
+  float* stats_out;
   void* dq;
   void* dk;
   void* dv;

@@ -118,3 +118,36 @@ def test_causal_zero_rows_and_invariants(fab):
     do64 = to_np64(do)
     np.testing.assert_allclose(dv.sum(axis=2), do64.reshape(1, 2, 2, 150, 64).sum(axis=(2, 3)),
                                rtol=1e-4, atol=1e-4)
+
+
+@pytest.mark.parametrize("dt,D,causal,window", [("bf16", 128, True, 0), ("fp16", 64, False, 40),
+                                                ("fp32", 64, True, 0)])
+def test_step_entry_points(fab, dt, D, causal, window):
+    """fab_bwd_preprocess, then fab_bwd_dkdv and fab_bwd_dq on their own (the calls the bench
+    times per kernel), against the oracle; fab_bwd itself folds step 1 into its dQ kernel on
+    the 16-bit path, so this route is checked separately."""
+    import ctypes
+    import torch
+    w = workloads.Workload(f"steps_{dt}", dt, 1, 4, 2, 230, 190, D, causal, seed=91, window=window)
+    say(f"[case] step entry points {dt} D={D} causal={causal} window={window}")
+    q, k, v, do = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
+    o, lse = fab.fwd(qd, kd, vd, causal=causal, scale=w.scale, window_size=window)
+    code = fab._dtype_code(qd)
+    nb = fab.bwd_workspace_bytes(w.B, w.H, w.H_kv, w.Sq, w.Sk, D, code)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    L = fab.lib()
+    st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    dims = (w.B, w.H, w.H_kv, w.Sq, w.Sk, D, code, int(causal), window, float(w.scale), st)
+    assert L.fab_bwd_preprocess(dod.data_ptr(), o.data_ptr(), lse.data_ptr(), ws.data_ptr(), nb,
+                                w.B, w.H, w.Sq, D, code, st) == 0
+    assert L.fab_bwd_dkdv(dod.data_ptr(), qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), ws.data_ptr(),
+                          nb, dk.data_ptr(), dv.data_ptr(), *dims) == 0
+    assert L.fab_bwd_dq(dod.data_ptr(), qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), ws.data_ptr(),
+                        nb, dq.data_ptr(), *dims) == 0
+    torch.cuda.synchronize()
+    ref = oracle.attention_grads(q, k, v, do, causal, w.scale, window=window)
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert_close(name, to_np64(g), ref[name], dt)
