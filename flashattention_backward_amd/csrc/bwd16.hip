@@ -43,9 +43,11 @@ struct Dkdv16 {
   static constexpr int SPARE = Dma::kSpare ? 1024 : 0;  // target of padding loads
   static constexpr int LDS = STAGES * BUF + VT + SPARE;
   static constexpr int RED = 2 * 64 * HD * 4;  // epilogue: two waves' partial dK or dV
+  static constexpr int OROW = HD * 2 + 16;     // epilogue: row pitch of the 16-bit output tile
+  static constexpr int OUT = 2 * 64 * OROW;    // epilogue: both key blocks' output rows
   // Loads each wave issues per stage (Q and dO; wave 0 adds the statistics).
   static constexpr int ISSUE = 2 * KMAX;
-  static_assert(RED <= LDS, "reduction must fit in the staging buffers");
+  static_assert(RED + OUT <= LDS, "reduction and output tiles must fit in the staging buffers");
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(TILE % 16 == 0 && VT % 16 == 0, "granule alignment");
 };
@@ -397,9 +399,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   mma_drain(dv[1]);
 
   // ---- epilogue: the qh = 1 waves hand their partial sums to the qh = 0 waves via LDS,
-  // which add, scale and store.  The accumulators of a wave pair have identical layouts, so
-  // the exchange is lane-major and conflict free.
+  // which add and scale them.  The accumulators of a wave pair have identical layouts, so the
+  // exchange is lane-major and conflict free.  A lane's sums lie down one column (16 keys of
+  // column 32 db + c32), so the qh = 0 waves write them, rounded to 16 bits, into a row-major
+  // tile in LDS and store that tile by whole rows: 16 bytes per lane and 1 KB per store
+  // instruction, instead of one 2-byte element per lane.  Rows are OROW bytes apart, so the
+  // two half-waves' 2-byte writes (rows 4 apart: 16 banks apart) never collide.
   float* red = reinterpret_cast<float*>(smem) + kb * (64 * HD);
+  char* const otile = smem + C::RED + kb * (64 * C::OROW);
   T* dKg = (T*)p.dk + kv_off;
   T* dVg = (T*)p.dv + kv_off;
 #pragma unroll
@@ -419,7 +426,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
     }
     __syncthreads();
     if (qh == 0) {
-      T* dst = pass == 0 ? dKg : dVg;
       const float sc = pass == 0 ? p.scale : 1.f;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
@@ -432,10 +438,22 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
             const f32x4 o = *reinterpret_cast<const f32x4*>(red + (slot * 64 + lane) * 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int n = nw0 + 32 * nb + 8 * r4 + 4 * hl + e;
-              if (n < Sk) dst[(size_t)n * HD + 32 * db + c32] = (T)((a[4 * r4 + e] + o[e]) * sc);
+              const int row = 32 * nb + 8 * r4 + 4 * hl + e;  // key nw0 + row
+              *reinterpret_cast<T*>(otile + row * C::OROW + 2 * (32 * db + c32)) =
+                  (T)((a[4 * r4 + e] + o[e]) * sc);
             }
           }
+      // the wave reads back only what it wrote: its LDS accesses complete in order
+      asm volatile("" ::: "memory");
+      T* const dst = pass == 0 ? dKg : dVg;
+      constexpr int CPR = HD / 8;  // 16-byte chunks per row
+#pragma unroll
+      for (int i = 0; i < CPR; ++i) {
+        const int q = 64 * i + lane, row = q / CPR, ch = q % CPR;
+        typedef T v8 __attribute__((ext_vector_type(8)));
+        const v8 val = *reinterpret_cast<const v8*>(otile + row * C::OROW + 16 * ch);
+        if (nw0 + row < Sk) *reinterpret_cast<v8*>(dst + (size_t)(nw0 + row) * HD + 8 * ch) = val;
+      }
     }
     __syncthreads();
   }
@@ -460,7 +478,9 @@ struct Dq16 {
   static constexpr int SPARE = Dma::kSpare ? 1024 : 0;  // target of padding loads
   static constexpr int LDS = STAGES * BUF + SPARE;
   static constexpr int ISSUE = 2 * KMAX;  // loads each wave issues per stage
+  static constexpr int OROW = HD * 2 + 16;  // epilogue: row pitch of the 16-bit output tile
   static_assert(LDS <= 80 * 1024, "two workgroups per CU");
+  static_assert(4 * 32 * OROW <= LDS, "the output tiles of the four waves fit the staging buffers");
 };
 
 template <class T, int HD, int NB>
@@ -658,17 +678,33 @@ __global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(const BwdParams p) {
     barrier_lds();
     cb = cb == STAGES - 1 ? 0 : cb + 1;
   }
-  wait_vm_all();  // no prefetch may still be writing LDS when the workgroup ends
+  wait_vm_all();  // no prefetch of this wave is still writing LDS ...
+  barrier_lds();  // ... nor of any other: the stage buffers are free for the output tiles
 
+  // ---- epilogue: dQ = scale * acc.  A lane's values lie down one column (16 rows of column
+  // 32 db + c32), so each wave writes its 32 rows, rounded to 16 bits, into a row-major tile
+  // of its own in LDS and stores that by whole rows: 16 bytes per lane instead of one 2-byte
+  // element.  Rows are OROW bytes apart, so the two half-waves' writes (rows 4 apart: 16 banks
+  // apart) never collide.
   mma_drain(dq);
-  T* dQg = (T*)p.dq + q_off * HD;
+  char* const otile = smem + w * (32 * C::OROW);
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int mr = mw0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-      if (mr < Sq) dQg[(size_t)mr * HD + 32 * db + c32] = (T)(dq[db][r] * p.scale);
+      const int row = 8 * (r >> 2) + 4 * hl + (r & 3);
+      *reinterpret_cast<T*>(otile + row * C::OROW + 2 * (32 * db + c32)) = (T)(dq[db][r] * p.scale);
     }
+  asm volatile("" ::: "memory");  // the wave reads back only what it wrote, in order
+  T* dQg = (T*)p.dq + q_off * HD;
+  constexpr int CPR = HD / 8;  // 16-byte chunks per row
+#pragma unroll
+  for (int i = 0; i < CPR / 2; ++i) {
+    const int q = 64 * i + lane, row = q / CPR, ch = q % CPR;
+    typedef T v8 __attribute__((ext_vector_type(8)));
+    const v8 val = *reinterpret_cast<const v8*>(otile + row * C::OROW + 16 * ch);
+    if (mw0 + row < Sq) *reinterpret_cast<v8*>(dQg + (size_t)(mw0 + row) * HD + 8 * ch) = val;
+  }
 }
 
 template <class T, int HD>

@@ -31,7 +31,9 @@ struct Fwd16 {
   static constexpr int KMAX = Dma::KMAX;
   static constexpr int SPARE = Dma::kSpare ? 1024 : 0;
   static constexpr int LDS = STAGES * BUF + SPARE;
+  static constexpr int OROW = HD * 2 + 16;  // epilogue: row pitch of the 16-bit output tile
   static_assert(LDS <= 80 * 1024, "two workgroups per CU");
+  static_assert(4 * 32 * OROW <= LDS, "the output tiles of the four waves fit the staging buffers");
 };
 
 template <class T, int HD>
@@ -204,25 +206,35 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(const FwdParams p) {
     barrier_lds();  // and nobody reads this one any more before it is overwritten
   }
 
-  // ---- epilogue: O = O^T / rowsum, written row by row (register r of block db holds
-  // column 32 db + 8 (r / 4) + 4 hl + r % 4 of this lane's row); LSE in natural log.  A row
-  // that may attend no key (possible with a window) gets O = 0 and LSE = log 0 = -inf.
+  // ---- epilogue: O = O^T / rowsum (register r of block db holds column 32 db + 8 (r / 4) +
+  // 4 hl + r % 4 of this lane's row); LSE in natural log.  A row that may attend no key
+  // (possible with a window) gets O = 0 and LSE = log 0 = -inf.  Each wave writes its 32 rows
+  // into a row-major tile of its own in LDS (the stage buffers are free: the loop ended on a
+  // barrier after every wave's loads) and stores it by whole rows, 16 bytes per lane.
   const float ltot = lsum + __shfl_xor(lsum, 32);
-  if (m < Sq) {
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    T* Og = (T*)p.o + (q_off + m) * HD;
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  char* const otile = smem + w * (32 * C::OROW);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        typedef T v4 __attribute__((ext_vector_type(4)));
-        const int d = 32 * db + 8 * q4 + 4 * hl;
-        *reinterpret_cast<v4*>(Og + d) =
-            v4{(T)(o[db][4 * q4] * inv), (T)(o[db][4 * q4 + 1] * inv),
-               (T)(o[db][4 * q4 + 2] * inv), (T)(o[db][4 * q4 + 3] * inv)};
-      }
-    if (hl == 0) p.lse[q_off + m] = (mrun + __log2f(ltot)) * kLn2;
+    for (int q4 = 0; q4 < 4; ++q4) {
+      typedef T v4 __attribute__((ext_vector_type(4)));
+      const int d = 32 * db + 8 * q4 + 4 * hl;
+      *reinterpret_cast<v4*>(otile + c32 * C::OROW + 2 * d) =
+          v4{(T)(o[db][4 * q4] * inv), (T)(o[db][4 * q4 + 1] * inv),
+             (T)(o[db][4 * q4 + 2] * inv), (T)(o[db][4 * q4 + 3] * inv)};
+    }
+  asm volatile("" ::: "memory");  // the wave reads back only what it wrote, in order
+  T* const Og = (T*)p.o + q_off * HD;
+  constexpr int CPR = HD / 8;  // 16-byte chunks per row
+#pragma unroll
+  for (int i = 0; i < CPR / 2; ++i) {
+    const int q = 64 * i + lane, row = q / CPR, ch = q % CPR;
+    typedef T v8 __attribute__((ext_vector_type(8)));
+    const v8 val = *reinterpret_cast<const v8*>(otile + row * C::OROW + 16 * ch);
+    if (mw0 + row < Sq) *reinterpret_cast<v8*>(Og + (size_t)(mw0 + row) * HD + 8 * ch) = val;
   }
+  if (m < Sq && hl == 0) p.lse[q_off + m] = (mrun + __log2f(ltot)) * kLn2;
 }
 
 template <class T, int HD>
