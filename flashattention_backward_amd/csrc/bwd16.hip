@@ -22,12 +22,12 @@ namespace fab {
 // =======================================================================================
 // dK, dV: key-tile outer (boostr flash_bwd.rs "Step 2": one workgroup per tile of keys).
 // A workgroup owns BN = 128 keys of one (batch, kv head) and walks every query head of the
-// group and every 64-row query tile the causal mask lets reach its keys.  Its 4 waves form a
-// 2 x 2 grid: wave (kb, qh) owns keys [64 kb, 64 kb + 64) and the query rows [32 qh, 32 qh + 32)
-// of each tile, so every Q / dO element read from LDS feeds 64 keys.  K and V sit in LDS for
-// the workgroup's life (the register file is taken by the dK, dV accumulators and the score
-// tiles); dK and dV accumulate in AGPRs and the two query halves are summed through LDS at
-// the end.
+// group and every 64-row query tile the mask (causal, window) lets reach its keys.  Its 4 waves
+// form a 2 x 2 grid: wave (kb, qh) owns keys [64 kb, 64 kb + 64) and the query rows
+// [32 qh, 32 qh + 32) of each tile, so every Q / dO element read from LDS feeds 64 keys.  A
+// wave's K fragments stay in registers and the V tile in LDS for the workgroup's life (there is
+// no room for V in registers beside the dK, dV accumulators and the score tiles); dK and dV
+// accumulate in AGPRs, and the two query halves are summed through LDS at the end.
 // =======================================================================================
 template <int HD>
 struct Dkdv16 {
@@ -460,11 +460,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
 }
 
 // =======================================================================================
-// dQ: query-tile outer.  A workgroup owns BM = 128 MB query rows of one (batch, head); wave w
-// owns MB 32-row blocks with their Q and dO fragments, LSE and D in registers.  Per step of
-// BN = 32 keys it recomputes S^T = K Q^T and dP^T = V dO^T (one query row per lane), forms
-// dS^T = P^T (dP^T - D) and adds dS K into the dQ accumulators.  K and V tiles stream through
-// a three-stage LDS ring.
+// dQ: query-tile outer.  A workgroup owns BM = 128 query rows of one (batch, head); wave w
+// owns 32 of them, with their Q and dO fragments, LSE and D in registers (one query row per
+// lane).  Per step of BN = 32 NB keys it recomputes S^T = K Q^T and dP^T = V dO^T, forms
+// dS^T = P^T (dP^T - D) and adds dS K into the dQ accumulators.  K and V tiles stream
+// through a ring of LDS stages (three for 32-key steps, two for 64-key steps), which keeps
+// two workgroups, i.e. two waves per SIMD, on a CU.  On fab_bwd's path the kernel also forms
+// its rows' D and base-2 LSE (step 1) and writes them for the dK/dV kernel.
 // =======================================================================================
 template <int HD, int NB>
 struct Dq16 {
