@@ -54,9 +54,12 @@ constexpr long long kMaxElems = (1LL << 31) - 1;
 
 size_t elem_size(int dt) { return dt == FAB_F32 ? 4 : 2; }
 
-// bf16 / fp16 at head dims 32 to 128 run the tiled kernels (fwd16.hip, bwd16.hip); fp32, and
-// bf16 / fp16 at head dim 256, run the generic ones (fwd.hip, bwd_dkdv.hip, bwd_dq.hip).
+// Which kernels run: bf16 / fp16 take the tiled dQ kernel at every head dim, and the tiled
+// dK/dV and forward kernels up to head dim 128 (fwd16.hip, bwd16.hip); fp32, and the dK/dV and
+// forward of bf16 / fp16 at head dim 256, take the generic ones (fwd.hip, bwd_dkdv.hip,
+// bwd_dq.hip).
 bool tiled(int dtype, int D) { return dtype != FAB_F32 && D <= 128; }
+bool tiled_dq(int dtype) { return dtype != FAB_F32; }
 
 fab_status check_common(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype) {
   if (dtype != FAB_F32 && dtype != FAB_F16 && dtype != FAB_BF16)
@@ -209,7 +212,7 @@ hipError_t launch_step2(const fab::BwdParams& p, int dtype, int D, hipStream_t s
     log_launch(*li);
   }
   if (dq) {
-    e = tiled(dtype, D) ? fab::launch_bwd_dq16(p, dtype, D, s, li) : fab::launch_bwd_dq(p, dtype, D, s, li);
+    e = tiled_dq(dtype) ? fab::launch_bwd_dq16(p, dtype, D, s, li) : fab::launch_bwd_dq(p, dtype, D, s, li);
     if (e != hipSuccess) return e;
     log_launch(*li);
   }
@@ -319,15 +322,14 @@ fab_status fab_bwd(const void* dO, const void* q, const void* k, const void* v,
   fab::LaunchInfo li;
   const fab::BwdParams p =
       bwd_params(dO, q, k, v, workspace, dq, dk, dv, B, H, H_kv, Sq, Sk, causal, window_size, scale);
-  if (tiled(dtype, D)) {
+  if (tiled_dq(dtype)) {
     // Step 1 runs inside the dQ kernel, which therefore goes first: it writes the row
     // statistics the dK/dV kernel then reads from the workspace.
     fab::BwdParams pq = p;
     pq.o = o; pq.lse = lse; pq.stats_out = static_cast<float*>(workspace);
     FAB_TRY(launched(fab::launch_bwd_dq16(pq, dtype, D, s, &li), "bwd_dq"));
     log_launch(li);
-    FAB_TRY(launched(fab::launch_bwd_dkdv16(p, dtype, D, s, &li), "bwd_dkdv"));
-    log_launch(li);
+    FAB_TRY(launched(launch_step2(p, dtype, D, s, true, false, &li), "bwd_dkdv"));
     return FAB_OK;
   }
   const fab::PreParams pp = pre_params(dO, o, lse, workspace, B, H, Sq);

@@ -474,19 +474,22 @@ struct Dq16 {
   static constexpr int BM = 128, BN = 32 * NB;  // one 32-row block per wave, NB key blocks
   static constexpr int TILE = L::bytes(BN);     // one K or V tile
   static constexpr int BUF = 2 * TILE;
-  static constexpr int STAGES = NB == 1 ? 3 : 2;  // two workgroups per CU either way
+  static constexpr int STAGES = NB == 1 ? 3 : 2;
   typedef TileDma<bf16, HD, BN> Dma;  // (the element type only sets the row size)
   static constexpr int KMAX = Dma::KMAX;
   static constexpr int SPARE = Dma::kSpare ? 1024 : 0;  // target of padding loads
   static constexpr int LDS = STAGES * BUF + SPARE;
   static constexpr int ISSUE = 2 * KMAX;  // loads each wave issues per stage
   static constexpr int OROW = HD * 2 + 16;  // epilogue: row pitch of the 16-bit output tile
-  static_assert(LDS <= 80 * 1024, "two workgroups per CU");
+  // Two workgroups (two waves per SIMD) per CU up to head dim 128; at 256 the Q, dO fragments
+  // and dQ accumulators of a wave take more than half the register file, so one.
+  static constexpr int WG_PER_CU = HD <= 128 ? 2 : 1;
+  static_assert(LDS <= 160 * 1024 / WG_PER_CU, "LDS per workgroup");
   static_assert(4 * 32 * OROW <= LDS, "the output tiles of the four waves fit the staging buffers");
 };
 
 template <class T, int HD, int NB>
-__global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(const BwdParams p) {
+__global__ __launch_bounds__(256, (HD <= 128 ? 2 : 1)) void bwd_dq16_kernel(const BwdParams p) {
   typedef Dq16<HD, NB> C;
   typedef typename Frag<T>::type F;
   constexpr int NC = HD / 16, NDB = HD / 32;
@@ -753,7 +756,8 @@ static hipError_t dq_hd(const BwdParams& p, int hd, hipStream_t s, LaunchInfo* i
     case 32: return go_dq<T, 32>(p, s, info);
     case 64: return go_dq<T, 64>(p, s, info);
     case 96: return go_dq<T, 96>(p, s, info);
-    default: return go_dq<T, 128>(p, s, info);
+    case 128: return go_dq<T, 128>(p, s, info);
+    default: return go_dq<T, 256>(p, s, info);
   }
 }
 

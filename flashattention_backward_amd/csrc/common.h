@@ -70,6 +70,10 @@ __device__ __forceinline__ void mma_a(f32x16& acc, const f16x8& a, const f16x8& 
 // Wait states between the last accumulating MFMA and any other access to its registers
 // (more than the 8 passes plus the read latency of a 32x32x16 MFMA).  Every accumulator is an
 // operand, so no accumulating MFMA can be scheduled after the wait and no read before it.
+__device__ __forceinline__ void mma_drain(f32x16 (&a)[8]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]),
+               "+a"(a[4]), "+a"(a[5]), "+a"(a[6]), "+a"(a[7]));
+}
 __device__ __forceinline__ void mma_drain(f32x16 (&a)[4]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]));
 }
@@ -232,6 +236,30 @@ struct TileLayout<64> {
   __device__ static __forceinline__ void granule(int gi, int& r, int& c) {
     r = gi >> 3;
     c = (gi & 7) ^ swz64(r);
+  }
+};
+
+// D=256: the same grouping with 512-byte rows.  Rows of a group are 576 B apart (16 banks) and
+// groups 2320 B apart (580 dwords, 4 mod 16), so a b128 read of 16 rows and a transposed
+// half-wave read (4 rows x 32 B) both hit distinct banks.
+template <>
+struct TileLayout<256> {
+  static constexpr int ROWB = 512;
+  static constexpr int SLOT = 576, GROUP = 2320;
+  static constexpr int GPG = GROUP / 16;  // 145
+  static constexpr int bytes(int rows) { return rows / 4 * GROUP; }
+  static constexpr int rows(int n) { return n / 4 * GROUP; }
+  __device__ static __forceinline__ int off(int r, int c) {
+    return (r >> 2) * GROUP + (r & 3) * SLOT + 16 * c;
+  }
+  // gap granules (4 after each row, 1 after the group) repeat chunks of the row before them
+  __device__ static __forceinline__ void granule(int gi, int& r, int& c) {
+    const int g = gi / GPG, q = gi - g * GPG;
+    const int b = min(q / (SLOT / 16), 3);
+    c = q - b * (SLOT / 16);
+    if (c >= 32) c -= 32;
+    if (c >= 32) c -= 32;
+    r = 4 * g + b;
   }
 };
 
