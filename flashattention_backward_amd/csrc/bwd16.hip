@@ -22,29 +22,35 @@ namespace fab {
 // =======================================================================================
 // dK, dV: key-tile outer (boostr flash_bwd.rs "Step 2": one workgroup per tile of keys).
 // A workgroup owns BN = 128 keys of one (batch, kv head) and walks every query head of the
-// group and every 64-row query tile the mask (causal, window) lets reach its keys.  Its 4 waves
-// form a 2 x 2 grid: wave (kb, qh) owns keys [64 kb, 64 kb + 64) and the query rows
-// [32 qh, 32 qh + 32) of each tile, so every Q / dO element read from LDS feeds 64 keys.  A
-// wave's K fragments stay in registers and the V tile in LDS for the workgroup's life (there is
-// no room for V in registers beside the dK, dV accumulators and the score tiles); dK and dV
-// accumulate in AGPRs, and the two query halves are summed through LDS at the end.
+// group and every query tile (BM rows) the mask (causal, window) lets reach its keys.  Up to
+// head dim 128 its 4 waves form a 2 x 2 grid: wave (kb, qh) owns keys [64 kb, 64 kb + 64) and
+// the query rows [32 qh, 32 qh + 32) of each 64-row tile, so every Q / dO element read from LDS
+// feeds 64 keys.  At head dim 256 the dK, dV accumulators of 64 keys would not fit, so the grid
+// is 4 x 1: wave kb owns keys [32 kb, 32 kb + 32) and all of a 32-row tile.  A wave's K
+// fragments stay in registers and the V tile in LDS for the workgroup's life (there is no room
+// for V in registers beside the dK, dV accumulators and the score tiles); dK and dV accumulate
+// in AGPRs, and with two query halves they are summed through LDS at the end.
 // =======================================================================================
 template <int HD>
 struct Dkdv16 {
   typedef TileLayout<HD> L;
-  static constexpr int BN = 128, BM = 64;
+  // Wave grid: KG groups of keys x QH halves of the query tile.  Up to head dim 128 a wave owns
+  // KB = 2 blocks of 32 keys and half of a 64-row query tile (2 x 2 grid); at 256 its dK, dV
+  // accumulators allow one block, so a wave owns 32 keys and all of a 32-row tile (4 x 1 grid).
+  static constexpr int KB = HD <= 128 ? 2 : 1, QH = KB, KG = 4 / QH;
+  static constexpr int BN = 128, BM = 32 * QH;
   static constexpr int TILE = L::bytes(BM);    // one Q or dO tile
   static constexpr int STATS = 1024;           // {lse2, D} of 128 rows (one wave-wide load)
   static constexpr int BUF = 2 * TILE + STATS; // one stage: Q, dO, stats
   static constexpr int VT = L::bytes(BN);      // V tile of the workgroup
-  static constexpr int STAGES = 3;             // tiles in flight: current + 2 prefetched
+  static constexpr int STAGES = HD <= 128 ? 3 : 2;  // tiles in flight: current + prefetched
   typedef TileDma<bf16, HD, BM> Dma;           // (the element type only sets the row size)
   static constexpr int KMAX = Dma::KMAX;
   static constexpr int SPARE = Dma::kSpare ? 1024 : 0;  // target of padding loads
   static constexpr int LDS = STAGES * BUF + VT + SPARE;
-  static constexpr int RED = 2 * 64 * HD * 4;  // epilogue: two waves' partial dK or dV
+  static constexpr int RED = QH > 1 ? 2 * 64 * HD * 4 : 0;  // epilogue: partial dK or dV exchange
   static constexpr int OROW = HD * 2 + 16;     // epilogue: row pitch of the 16-bit output tile
-  static constexpr int OUT = 2 * 64 * OROW;    // epilogue: both key blocks' output rows
+  static constexpr int OUT = BN * OROW;        // epilogue: the tile's output rows
   // Loads each wave issues per stage (Q and dO; wave 0 adds the statistics).
   static constexpr int ISSUE = 2 * KMAX;
   static_assert(RED + OUT <= LDS, "reduction and output tiles must fit in the staging buffers");
@@ -59,7 +65,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   typedef TileDma<T, HD, Dkdv16<HD>::BM> Dma;
   constexpr int NC = HD / 16, NDB = HD / 32;
   static_assert(C::KMAX <= NC, "a tile's prefetch is spread over the head-dim slices");
-  constexpr int BM = C::BM, BN = C::BN;
+  constexpr int BM = C::BM, BN = C::BN, KB = C::KB, STAGES = C::STAGES;
   typedef typename C::L L;
   constexpr unsigned ROWB = HD * sizeof(T);
 
@@ -70,7 +76,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
   const int lane = tid & 63, hl = lane >> 5, c32 = lane & 31;
-  const int kb = w & 1, qh = w >> 1;
+  const int kb = w % C::KG, qh = w / C::KG;
 
   const WorkItem wi = map_work(blockIdx.x, p.n_units, p.units_per_xcd);
   const int b = wi.unit / p.H_kv, g = wi.unit % p.H_kv;
@@ -83,18 +89,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
 
   // ---- V tile -> LDS once for the workgroup's life; K fragments -> registers
   load_tile<T, HD, BN>(vtile, Vg, n0, Sk - 1, w, 4, lane);
-  const int nw0 = n0 + 64 * kb;
-  F kf[2][NC];
+  const int nw0 = n0 + 32 * KB * kb;
+  F kf[KB][NC];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
+  for (int nb = 0; nb < KB; ++nb) {
     const int n = min(nw0 + 32 * nb + c32, Sk - 1);
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) kf[nb][cc] = ld8(Kg + (size_t)n * HD + 16 * cc + 8 * hl);
   }
 
-  f32x16 dk[2][NDB], dv[2][NDB];
+  f32x16 dk[KB][NDB], dv[KB][NDB];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int nb = 0; nb < KB; ++nb)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       dk[nb][db] = f32x16{};
@@ -117,10 +123,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
       const int col = 32 * db + 16 * dh + 4 * (gi16 & 3);
       t_off[db][sec] = L::off(r, col >> 3) + 2 * (col & 7);
     }
-  // B operand of dP = dO V^T: V rows 64 kb + 32 nb + c32 have the same layout offsets as the
+  // B operand of dP = dO V^T: V rows 32 (KB kb + nb) + c32 have the same layout offsets as the
   // A operand rows 32 qh + c32 shifted by a whole number of row groups, so they are a_off
   // plus a wave constant.
-  const char* const vrows = vtile + L::rows(64 * kb) - L::rows(32 * qh);
+  const char* const vrows = vtile + L::rows(32 * KB * kb) - L::rows(32 * qh);
 
   // ---- iteration space: every query head of the group and every query tile holding a row
   // that may attend one of these keys (rows [r_lo, r_hi]).  Tiles run from the last one
@@ -134,10 +140,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   const int i_first = r_lo / BM, i_last = r_hi / BM;
   const int per = r_hi >= r_lo ? i_last - i_first + 1 : 0;
   const int total = G * per;
-  // The wave's 32 rows from mw0 see all of its 64 keys from nw0 iff kr.hi(mw0) >= nw0 + 63
-  // and kr.lo(mw0 + 31) <= nw0, i.e. iff full_lo <= mw0 <= full_hi:
-  const int full_lo = nw0 + 63 > Sk - 1 ? (1 << 30)
-                      : p.causal ? nw0 + 63 : (p.win > 0 ? nw0 + 64 - p.win : -(1 << 30));
+  // The wave's 32 rows from mw0 see all of its 32 KB keys from nw0 iff
+  // kr.hi(mw0) >= nw0 + 32 KB - 1 and kr.lo(mw0 + 31) <= nw0, i.e. iff full_lo <= mw0 <= full_hi:
+  const int full_lo = nw0 + 32 * KB - 1 > Sk - 1 ? (1 << 30)
+                      : p.causal ? nw0 + 32 * KB - 1 : (p.win > 0 ? nw0 + 32 * KB - p.win : -(1 << 30));
   const int full_hi = p.win > 0 ? nw0 + p.win - 32 : (1 << 30);
 
   // Buffer resources over the rows of the group's query heads (Q, dO) and their row
@@ -177,11 +183,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
     for (int k = 0; k < C::KMAX; ++k) issue_part(buf, k, qs, ss);
   };
 
-  // Ring of STAGES tile buffers: step s computes on buffer s % 3 while the tiles of steps
-  // s + 1 and s + 2 are in flight.
-  issue(smem);
-  issue(smem + C::BUF);
-  wait_vm_le<C::ISSUE>();  // V, K and stage 0 have landed
+  // Ring of STAGES tile buffers: step s computes on buffer s % STAGES while the tiles of the
+  // next STAGES - 1 steps are in flight.
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st) issue(smem + st * C::BUF);
+  wait_vm_le<C::ISSUE * (STAGES - 2)>();  // V, K and stage 0 have landed
   barrier_lds();
 
   const float mask_s = p.mask_s;
@@ -219,35 +225,35 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   load_step_operands(smem);
 
   // One step on stage `cur`; `nb1` is the stage of the next step and `nxt` the stage being
-  // prefetched (step s + 2).  The workgroup barrier that ends the step sits before its last
-  // eight MFMAs: by then every read of `cur` has completed, and the next step's operands are
-  // read from `nb1` while those MFMAs run.
+  // prefetched (step s + STAGES - 1; with two stages it is `nb1` itself).  The workgroup
+  // barrier that ends the step sits before its last MFMAs: by then every read of `cur` has
+  // completed, and the next step's operands are read from `nb1` while those MFMAs run.
   auto step_body = [&](const char* __restrict__ cur, const char* __restrict__ vrows,
-                       char* __restrict__ nxt, const char* __restrict__ nb1, int m0) {
+                       char* __restrict__ nxt, const char* nb1, int m0) {
     unsigned pq_soff, pst_soff;
     next_offsets(pq_soff, pst_soff);
     const int mw0 = m0 + 32 * qh;
 
-    // ---- S = Q K^T for both key blocks; the prefetch of step s + 2 is spread over it, one
-    // instruction per head-dim slice, so the wave never stalls on a burst of loads.
-    f32x16 S[2], dP[2];
+    // ---- S = Q K^T for the wave's key blocks; the prefetch is spread over it, one instruction
+    // per head-dim slice, so the wave never stalls on a burst of loads.
+    f32x16 S[KB], dP[KB];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) S[nb] = f32x16{};
+    for (int nb = 0; nb < KB; ++nb) S[nb] = f32x16{};
     // Operands of dP = dO V^T stream through a window LEAD head-dim slices deep; the first
     // LEAD slices are read here, under the S MFMAs (LDS latency under load is several MFMAs).
     constexpr int LEAD = NC >= 8 ? 3 : 2;
-    F ad[NC], bv0[NC], bv1[NC];
+    F ad[NC], bv[KB][NC];
     auto read_dp_operands = [&](int cc) {
       ad[cc] = lds_frag<T>(cur + C::TILE, a_off[cc]);
-      bv0[cc] = lds_frag<T>(vrows, a_off[cc]);
-      bv1[cc] = lds_frag<T>(vrows + L::rows(32), a_off[cc]);
+#pragma unroll
+      for (int nb = 0; nb < KB; ++nb) bv[nb][cc] = lds_frag<T>(vrows + L::rows(32 * nb), a_off[cc]);
     };
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
       if (cc < C::KMAX) issue_part(nxt, cc, pq_soff, pst_soff);
       if (cc < LEAD) read_dp_operands(cc);
-      mma(S[0], aq[cc], kf[0][cc]);
-      mma(S[1], aq[cc], kf[1][cc]);
+#pragma unroll
+      for (int nb = 0; nb < KB; ++nb) mma(S[nb], aq[cc], kf[nb][cc]);
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -258,7 +264,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
     if (mw0 < full_lo || mw0 > full_hi) {
       const int m_base = mw0 + 4 * hl;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < KB; ++nb) {
         const int n = nw0 + 32 * nb + c32;
         const int a = n < Sk ? kr.rows_lo(n) - m_base : (1 << 30);
         const int z = kr.rows_hi(n) - m_base;
@@ -275,8 +281,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
     // 16-bit copy, the A operand of dV += P^T dO) while the MFMAs run.  Fragment (nb, ks)
     // holds registers 8 ks .. 8 ks + 7 of block nb.  The dP MFMAs are volatile asm and every
     // exponential is pinned between them with order_point(), so the interleave is exact.
-    F pa[2][2], da[2][2];
-    constexpr int PER_CC = (32 + NC - 1) / NC;  // exponentials per head-dim slice
+    F pa[KB][2], da[KB][2];
+    constexpr int NE = 16 * KB;                  // exponentials of a lane
+    constexpr int PER_CC = (NE + NC - 1) / NC;   // exponentials per head-dim slice
+    constexpr int PER_NB = (PER_CC + KB - 1) / KB;  // ... after each of its MFMAs
     auto pexp = [&](int e) {
       const int nb = e >> 4, r = e & 15;
       float x = fast_exp2(S[nb][r] * p.scale_log2 - l2[r]);
@@ -287,16 +295,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
       if (cc + LEAD < NC) read_dp_operands(cc + LEAD);
-      if (cc == 0) mma_v0(dP[0], ad[cc], bv0[cc]);
-      else mma_v(dP[0], ad[cc], bv0[cc]);
 #pragma unroll
-      for (int k = 0; k < PER_CC / 2; ++k)
-        if (cc * PER_CC + k < 32) pexp(cc * PER_CC + k);
-      if (cc == 0) mma_v0(dP[1], ad[cc], bv1[cc]);
-      else mma_v(dP[1], ad[cc], bv1[cc]);
+      for (int nb = 0; nb < KB; ++nb) {
+        if (cc == 0) mma_v0(dP[nb], ad[cc], bv[nb][cc]);
+        else mma_v(dP[nb], ad[cc], bv[nb][cc]);
 #pragma unroll
-      for (int k = PER_CC / 2; k < PER_CC; ++k)
-        if (cc * PER_CC + k < 32) pexp(cc * PER_CC + k);
+        for (int k = nb * PER_NB; k < (nb + 1) * PER_NB && k < PER_CC; ++k)
+          if (cc * PER_CC + k < NE) pexp(cc * PER_CC + k);
+      }
     }
     mma_vdrain(dP);
     __builtin_amdgcn_sched_barrier(0);
@@ -317,18 +323,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
     F bo[NDB], bq[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) bo[db] = b_do(db, 0);
-    constexpr int PER_MMA = (16 + 2 * NDB - 1) / (2 * NDB);  // dS elements per MFMA of a 16-row slice
+    constexpr int PER_MMA = (8 + NDB - 1) / NDB;  // dS elements per MFMA of a 16-row slice
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       bq[db] = b_q(db, 0);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < KB; ++nb) {
         if (db == 0) mma_a<true>(dv[nb][db], pa[nb][0], bo[db]);  // first use of pa[nb][0]
         else mma_a(dv[nb][db], pa[nb][0], bo[db]);
 #pragma unroll
         for (int k = 0; k < PER_MMA; ++k) {
-          const int e = (2 * db + nb) * PER_MMA + k;  // 0..15 over rows 0..15 of both blocks
-          if (e < 16) ds(e & 1, e >> 1);
+          const int e = (KB * db + nb) * PER_MMA + k;  // rows 0..7 of every block
+          if (e < 8 * KB) ds(e % KB, e / KB);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -338,13 +344,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
     for (int db = 0; db < NDB; ++db) {
       bo[db] = b_do(db, 1);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < KB; ++nb) {
         if (db == 0) mma_a<true>(dk[nb][db], da[nb][0], bq[db]);  // first use of da[nb][0]
         else mma_a(dk[nb][db], da[nb][0], bq[db]);
 #pragma unroll
         for (int k = 0; k < PER_MMA; ++k) {
-          const int e = (2 * db + nb) * PER_MMA + k;
-          if (e < 16) ds(e & 1, 8 + (e >> 1));
+          const int e = (KB * db + nb) * PER_MMA + k;
+          if (e < 8 * KB) ds(e % KB, 8 + e / KB);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -354,7 +360,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
     for (int db = 0; db < NDB; ++db) {
       bq[db] = b_q(db, 1);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < KB; ++nb) {
         if (db == 0) mma_a<true>(dv[nb][db], pa[nb][1], bo[db]);
         else mma_a(dv[nb][db], pa[nb][1], bo[db]);
       }
@@ -362,14 +368,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
     }
     // ---- end of the step for the workgroup: the next stage has landed (the loads of the one
     // after it may stay in flight) and no wave reads `cur` any more.
-    wait_vm_le<C::ISSUE>();
+    wait_vm_le<C::ISSUE * (STAGES - 2)>();
     barrier_lds();
     load_step_operands(nb1);
     // ---- dK += dS^T Q for rows 16..31 while the next step's operands arrive.
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < KB; ++nb) {
         if (db == 0) mma_a<true>(dk[nb][db], da[nb][1], bq[db]);
         else mma_a(dk[nb][db], da[nb][1], bq[db]);
       }
@@ -380,8 +386,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   int cb = 0;  // buffer of step s
   int it = i_last, hh = 0;
   for (int s = 0; s < total; ++s) {
-    const int nb1 = cb == 2 ? 0 : cb + 1;  // (s + 1) % 3
-    const int nb2 = cb >= 1 ? cb - 1 : 2;  // (s + 2) % 3
+    const int nb1 = cb == STAGES - 1 ? 0 : cb + 1;                     // (s + 1) % STAGES
+    const int nb2 = STAGES == 2 ? nb1 : (cb >= 1 ? cb - 1 : STAGES - 1);  // (s + STAGES - 1) % STAGES
     step_body(smem + cb * C::BUF, vrows, smem + nb2 * C::BUF, smem + nb1 * C::BUF, it * BM);
     cb = nb1;
     if (++hh == G) {
@@ -393,49 +399,57 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   wait_vm_all();
   barrier_lds();
 
-  mma_drain(dk[0]);
-  mma_drain(dk[1]);
-  mma_drain(dv[0]);
-  mma_drain(dv[1]);
+#pragma unroll
+  for (int nb = 0; nb < KB; ++nb) {
+    mma_drain(dk[nb]);
+    mma_drain(dv[nb]);
+  }
 
-  // ---- epilogue: the qh = 1 waves hand their partial sums to the qh = 0 waves via LDS,
-  // which add and scale them.  The accumulators of a wave pair have identical layouts, so the
-  // exchange is lane-major and conflict free.  A lane's sums lie down one column (16 keys of
-  // column 32 db + c32), so the qh = 0 waves write them, rounded to 16 bits, into a row-major
-  // tile in LDS and store that tile by whole rows: 16 bytes per lane and 1 KB per store
-  // instruction, instead of one 2-byte element per lane.  Rows are OROW bytes apart, so the
-  // two half-waves' 2-byte writes (rows 4 apart: 16 banks apart) never collide.
-  float* red = reinterpret_cast<float*>(smem) + kb * (64 * HD);
-  char* const otile = smem + C::RED + kb * (64 * C::OROW);
+  // ---- epilogue.  With two query halves the qh = 1 waves hand their partial sums to the
+  // qh = 0 waves via LDS, which add them; the accumulators of a wave pair have identical
+  // layouts, so the exchange is lane-major and conflict free.  A lane's sums lie down one
+  // column (16 keys of column 32 db + c32), so the storing waves write them, scaled and rounded
+  // to 16 bits, into a row-major tile in LDS and store that tile by whole rows: 16 bytes per
+  // lane and 1 KB per store instruction, instead of one 2-byte element per lane.  Rows are
+  // OROW bytes apart, so the two half-waves' 2-byte writes (rows 4 apart: 16 banks apart)
+  // never collide.
+  char* const otile = smem + C::RED + kb * (32 * KB * C::OROW);
   T* dKg = (T*)p.dk + kv_off;
   T* dVg = (T*)p.dv + kv_off;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
-    if (qh == 1) {
+    if constexpr (C::QH > 1) {
+      float* red = reinterpret_cast<float*>(smem) + kb * (32 * KB * HD);
+      if (qh == 1) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < KB; ++nb)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+          for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x16& a = pass == 0 ? dk[nb][db] : dv[nb][db];
-            const int slot = (nb * NDB + db) * 4 + r4;
-            *reinterpret_cast<f32x4*>(red + (slot * 64 + lane) * 4) =
-                f32x4{a[4 * r4], a[4 * r4 + 1], a[4 * r4 + 2], a[4 * r4 + 3]};
-          }
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const f32x16& a = pass == 0 ? dk[nb][db] : dv[nb][db];
+              const int slot = (nb * NDB + db) * 4 + r4;
+              *reinterpret_cast<f32x4*>(red + (slot * 64 + lane) * 4) =
+                  f32x4{a[4 * r4], a[4 * r4 + 1], a[4 * r4 + 2], a[4 * r4 + 3]};
+            }
+      }
+      __syncthreads();
     }
-    __syncthreads();
     if (qh == 0) {
       const float sc = pass == 0 ? p.scale : 1.f;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < KB; ++nb)
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
             const f32x16& a = pass == 0 ? dk[nb][db] : dv[nb][db];
-            const int slot = (nb * NDB + db) * 4 + r4;
-            const f32x4 o = *reinterpret_cast<const f32x4*>(red + (slot * 64 + lane) * 4);
+            f32x4 o = f32x4{};
+            if constexpr (C::QH > 1) {
+              const float* red = reinterpret_cast<const float*>(smem) + kb * (32 * KB * HD);
+              const int slot = (nb * NDB + db) * 4 + r4;
+              o = *reinterpret_cast<const f32x4*>(red + (slot * 64 + lane) * 4);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int row = 32 * nb + 8 * r4 + 4 * hl + e;  // key nw0 + row
@@ -448,7 +462,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
       T* const dst = pass == 0 ? dKg : dVg;
       constexpr int CPR = HD / 8;  // 16-byte chunks per row
 #pragma unroll
-      for (int i = 0; i < CPR; ++i) {
+      for (int i = 0; i < KB * CPR / 2; ++i) {
         const int q = 64 * i + lane, row = q / CPR, ch = q % CPR;
         typedef T v8 __attribute__((ext_vector_type(8)));
         const v8 val = *reinterpret_cast<const v8*>(otile + row * C::OROW + 16 * ch);
@@ -746,7 +760,8 @@ static hipError_t dkdv_hd(const BwdParams& p, int hd, hipStream_t s, LaunchInfo*
     case 32: return go_dkdv<T, 32>(p, s, info);
     case 64: return go_dkdv<T, 64>(p, s, info);
     case 96: return go_dkdv<T, 96>(p, s, info);
-    default: return go_dkdv<T, 128>(p, s, info);
+    case 128: return go_dkdv<T, 128>(p, s, info);
+    default: return go_dkdv<T, 256>(p, s, info);
   }
 }
 

@@ -1,6 +1,5 @@
 // The generic path: fp32 inputs (v_mfma_f32_32x32x2f32: fp32 products and sums) at head dims
-// 32, 64, 96 and 128, and bf16 / fp16 inputs at head dim 256; bf16 and fp16 at head dims 32
-// to 128 use the tiled kernels of bwd16.hip.
+// 32, 64, 96 and 128; bf16 and fp16 inputs use the tiled dK/dV kernel of bwd16.hip.
 //
 // Main backward step for dK and dV (boostr flash_bwd.rs, "Step 2: Main backward kernel",
 // whose launch gives every workgroup one tile of keys: grid (batch*heads, ceil(Sk/BLOCK_N))
@@ -29,8 +28,7 @@ template <class T, int HD>
 struct DkdvCfg {
   static constexpr int NW = 4;
   static constexpr int BN = 32 * NW;                   // keys per workgroup
-  // query rows per step (32 where registers are tight: fp32 operands, head dim 256)
-  static constexpr int BM = (sizeof(T) == 4 || HD > 128) ? 32 : 64;
+  static constexpr int BM = sizeof(T) == 4 ? 32 : 64;  // query rows per step
   static constexpr int ES = sizeof(T);
   static constexpr int PAD = 16 / ES;                  // +16 bytes per LDS row
   static constexpr int LDR = HD + PAD;                 // row-major tile [BM][LDR]
@@ -216,17 +214,9 @@ static hipError_t go(const BwdParams& p, hipStream_t s, LaunchInfo* info) {
   return hipGetLastError();
 }
 
-template <class T>
-static hipError_t go16_generic(const BwdParams& p, int hd, hipStream_t s, LaunchInfo* info) {
-  (void)hd;  // bf16 / fp16: the one head dim without a tiled kernel
-  return go<T, 256>(p, s, info);
-}
-
-// fp32 inputs at head dims 32..128; bf16 and fp16 inputs at head dim 256, which the tiled
-// kernels do not cover.
+// fp32 inputs only; bf16 and fp16 inputs run the tiled dK/dV kernel of bwd16.hip.
 hipError_t launch_bwd_dkdv(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info) {
-  if (dt == kBF16) return go16_generic<bf16>(p, hd, s, info);
-  if (dt == kF16) return go16_generic<f16>(p, hd, s, info);
+  (void)dt;
   switch (hd) {
     case 32: return go<float, 32>(p, s, info);
     case 64: return go<float, 64>(p, s, info);

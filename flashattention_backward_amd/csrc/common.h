@@ -116,6 +116,9 @@ __device__ __forceinline__ void mma_v0(f32x16& acc, const f16x8& a, const f16x8&
 __device__ __forceinline__ void mma_vdrain(f32x16 (&a)[2]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(a[0]), "+v"(a[1]));
 }
+__device__ __forceinline__ void mma_vdrain(f32x16 (&a)[1]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(a[0]));
+}
 // Marks a point in the volatile-asm order by which x must have been computed.
 __device__ __forceinline__ void order_point(float& x) { asm volatile("" : "+v"(x)); }
 
