@@ -55,6 +55,16 @@ def assert_close(name: str, got: np.ndarray, ref: np.ndarray, dtype: str):
     assert fro <= tfro, f"{name}: relative Frobenius error {fro:.3e} > {tfro:g}"
 
 
+def window_span_ranges(c: int, e: int, S: int, W: int):
+    """For causal attention with a window of W keys over S positions, the rows and the keys of
+    the span [c, e) whose results the span's inputs alone determine: a row i sees keys
+    [i - W + 1, i], inside the span from i = c + W - 1 on (from 0 at the sequence's start);
+    a key j gets gradient from rows [j, j + W - 1], all such rows below e - W + 1 (below S at
+    the sequence's end).  Returns ((row_lo, row_hi), (key_lo, key_hi)), half-open."""
+    lo = c + W - 1 if c > 0 else 0
+    return (lo, e), (lo, e - W + 1 if e < S else S)
+
+
 def run_gpu(fab, q, k, v, do, causal, scale, window=0):
     """End-to-end HIP path: fwd then bwd, all inputs resident on cuda:0."""
     import torch

@@ -207,3 +207,33 @@ def test_window_invariants(causal):
                                (do * kept).reshape(B, H_kv, G, Sq, D).sum(axis=(2, 3)), atol=1e-12)
     lhs = (q * r["dq"]).reshape(B, H_kv, G, Sq, D).sum(axis=(2, 3, 4))
     np.testing.assert_allclose(lhs, (k * r["dk"]).sum(axis=(2, 3)), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("W", [1, 7, 16])
+def test_window_span_determines_its_rows_and_keys(W):
+    """What the maximum-size GPU test relies on: for causal attention with a window, the
+    oracle on a span of positions gives the full sequence's O, LSE, dQ on the span's exact
+    rows and dK, dV on its exact keys (window_span_ranges), at the start, inside, and at the
+    end of the sequence."""
+    from parity_helpers import window_span_ranges
+    B, H, H_kv, S, D = 1, 4, 2, 90, 8
+    q, k, v, do = inputs(B, H, H_kv, S, S, D, 290 + W)
+    full = attention_grads(q, k, v, do, True, 0.35, window=W)
+    n = 3 * W + 5
+    for c, e in ((0, n), (31, 31 + n), (S - n, S)):
+        (r0, r1), (k0, k1) = window_span_ranges(c, e, S, W)
+        assert r1 > r0 and k1 > k0
+        part = attention_grads(q[:, :, c:e], k[:, :, c:e], v[:, :, c:e], do[:, :, c:e], True, 0.35,
+                               window=W)
+        for key, a, b in (("o", r0, r1), ("lse", r0, r1), ("dq", r0, r1), ("dk", k0, k1), ("dv", k0, k1)):
+            np.testing.assert_allclose(part[key][:, :, a - c:b - c], full[key][:, :, a:b],
+                                       rtol=1e-12, atol=1e-13, err_msg=f"{key} span {c}:{e}")
+    # with W > 1, the row before and the key after those ranges differ: the ranges are tight
+    # (with W = 1 a row sees only its own key and every row and key of a span is exact)
+    if W > 1:
+        c, e = 31, 31 + n
+        (r0, _), (_, k1) = window_span_ranges(c, e, S, W)
+        part = attention_grads(q[:, :, c:e], k[:, :, c:e], v[:, :, c:e], do[:, :, c:e], True, 0.35,
+                               window=W)
+        assert not np.allclose(part["o"][:, :, r0 - 1 - c], full["o"][:, :, r0 - 1])
+        assert not np.allclose(part["dv"][:, :, k1 - c], full["dv"][:, :, k1])

@@ -17,7 +17,7 @@ import math
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "HEADLINE", "get", "make_inputs", "scaled"]
+__all__ = ["Workload", "WORKLOADS", "HEADLINE", "get", "make_inputs", "make_inputs_device", "scaled"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -116,3 +116,30 @@ def make_inputs(w: Workload):
         do *= np.float32(w.do_std)
     dt = _torch_dtype(w.dtype)
     return tuple(torch.from_numpy(x).to(dt).contiguous() for x in (q, k, v, do))
+
+
+def make_inputs_device(w: Workload, device):
+    """Return (q, k, v, do) drawn directly on ``device``, for shapes too large to draw on the
+    host (a tensor of 2**31 elements).  Recipe: torch's seeded device generator (Philox),
+    seeded with ``w.seed``, draws Q, K, V, dO in that order as standard normals in float32;
+    dO is multiplied by ``do_std``; each is rounded to ``w.dtype`` (round-to-nearest-even).
+    The oracle's inputs are slices of these very tensors copied to the host, so both sides
+    still see the same bits."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed)
+    dt = _torch_dtype(w.dtype)
+
+    def draw(shape, mul=1.0):
+        x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+        if mul != 1.0:
+            x.mul_(mul)
+        return x if dt == torch.float32 else x.to(dt)
+
+    qs = (w.B, w.H, w.Sq, w.D)
+    ks = (w.B, w.H_kv, w.Sk, w.D)
+    q = draw(qs)
+    k = draw(ks)
+    v = draw(ks)
+    do = draw(qs, w.do_std)
+    return q, k, v, do
