@@ -54,11 +54,9 @@ constexpr long long kMaxElems = (1LL << 31) - 1;
 
 size_t elem_size(int dt) { return dt == FAB_F32 ? 4 : 2; }
 
-// Which kernels run: bf16 / fp16 take the tiled backward kernels at every head dim
-// (bwd16.hip) and the tiled forward up to head dim 128 (fwd16.hip); fp32, and the forward of
-// bf16 / fp16 at head dim 256, take the generic ones (fwd.hip, bwd_dkdv.hip, bwd_dq.hip).
-bool tiled(int dtype, int D) { return dtype != FAB_F32 && D <= 128; }
-bool tiled_bwd(int dtype) { return dtype != FAB_F32; }
+// Which kernels run: bf16 / fp16 take the tiled kernels (fwd16.hip, bwd16.hip) at every head
+// dim; fp32 takes the generic ones (fwd.hip, bwd_dkdv.hip, bwd_dq.hip).
+bool tiled(int dtype) { return dtype != FAB_F32; }
 
 fab_status check_common(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype) {
   if (dtype != FAB_F32 && dtype != FAB_F16 && dtype != FAB_BF16)
@@ -206,12 +204,12 @@ hipError_t launch_step2(const fab::BwdParams& p, int dtype, int D, hipStream_t s
                         fab::LaunchInfo* li) {
   hipError_t e = hipSuccess;
   if (dkdv) {
-    e = tiled_bwd(dtype) ? fab::launch_bwd_dkdv16(p, dtype, D, s, li) : fab::launch_bwd_dkdv(p, dtype, D, s, li);
+    e = tiled(dtype) ? fab::launch_bwd_dkdv16(p, dtype, D, s, li) : fab::launch_bwd_dkdv(p, dtype, D, s, li);
     if (e != hipSuccess) return e;
     log_launch(*li);
   }
   if (dq) {
-    e = tiled_bwd(dtype) ? fab::launch_bwd_dq16(p, dtype, D, s, li) : fab::launch_bwd_dq(p, dtype, D, s, li);
+    e = tiled(dtype) ? fab::launch_bwd_dq16(p, dtype, D, s, li) : fab::launch_bwd_dq(p, dtype, D, s, li);
     if (e != hipSuccess) return e;
     log_launch(*li);
   }
@@ -268,7 +266,7 @@ fab_status fab_fwd(const void* q, const void* k, const void* v, void* o, float* 
   p.n_units = B * H_kv;
   p.units_per_xcd = units_per_xcd(p.n_units);
   fab::LaunchInfo li;
-  const hipError_t e = tiled(dtype, D) ? fab::launch_fwd16(p, dtype, D, (hipStream_t)stream, &li)
+  const hipError_t e = tiled(dtype) ? fab::launch_fwd16(p, dtype, D, (hipStream_t)stream, &li)
                                        : fab::launch_fwd(p, dtype, D, (hipStream_t)stream, &li);
   FAB_TRY(launched(e, "fwd"));
   log_launch(li);
@@ -321,7 +319,7 @@ fab_status fab_bwd(const void* dO, const void* q, const void* k, const void* v,
   fab::LaunchInfo li;
   const fab::BwdParams p =
       bwd_params(dO, q, k, v, workspace, dq, dk, dv, B, H, H_kv, Sq, Sk, causal, window_size, scale);
-  if (tiled_bwd(dtype)) {
+  if (tiled(dtype)) {
     // Step 1 runs inside the dQ kernel, which therefore goes first: it writes the row
     // statistics the dK/dV kernel then reads from the workspace.
     fab::BwdParams pq = p;

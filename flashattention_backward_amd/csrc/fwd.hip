@@ -1,6 +1,5 @@
 // The generic path: fp32 inputs (v_mfma_f32_32x32x2f32: fp32 products and sums) at head dims
-// 32, 64, 96 and 128, and bf16 / fp16 inputs at head dim 256; bf16 and fp16 at head dims 32
-// to 128 use the tiled forward of fwd16.hip.
+// 32, 64, 96 and 128; bf16 and fp16 inputs use the tiled forward of fwd16.hip.
 //
 // Supporting forward: O = softmax(scale Q K^T over the allowed keys) V and the row LSE
 // (natural log), which the backward consumes (boostr autograd_attention.rs,
@@ -204,17 +203,9 @@ static hipError_t go(const FwdParams& p, hipStream_t s, LaunchInfo* info) {
   return hipGetLastError();
 }
 
-template <class T>
-static hipError_t go16_generic(const FwdParams& p, int hd, hipStream_t s, LaunchInfo* info) {
-  (void)hd;  // bf16 / fp16: the one head dim without a tiled kernel
-  return go<T, 256>(p, s, info);
-}
-
-// fp32 inputs at head dims 32..128; bf16 and fp16 inputs at head dim 256, which the tiled
-// kernels do not cover.
+// fp32 inputs only; bf16 and fp16 inputs run the tiled forward of fwd16.hip.
 hipError_t launch_fwd(const FwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info) {
-  if (dt == kBF16) return go16_generic<bf16>(p, hd, s, info);
-  if (dt == kF16) return go16_generic<f16>(p, hd, s, info);
+  (void)dt;
   switch (hd) {
     case 32: return go<float, 32>(p, s, info);
     case 64: return go<float, 64>(p, s, info);

@@ -12,8 +12,9 @@
 // max, the rescale factor and the final normalisation are per-lane scalars.
 //
 // K and V tiles arrive by direct-to-LDS buffer loads into a double buffer (the prefetch of
-// the next tile is spread over the S MFMAs); 2 x 2 tiles of 64 rows fit two workgroups per
-// CU, i.e. two waves per SIMD.  Rescaling is lazy: O and the row sum are rescaled only when
+// the next tile is spread over the S MFMAs); up to head dim 128, 2 x 2 tiles of 64 rows fit
+// two workgroups per CU, i.e. two waves per SIMD; at 256 one workgroup fills the CU's LDS
+// and its waves have the whole register file for the 256-wide accumulators.  Rescaling is lazy: O and the row sum are rescaled only when
 // some row's maximum grew by more than 2^8 since the last rescale, so P <= 2^8 always.
 #include "common.h"
 #include "launch.h"
@@ -32,12 +33,13 @@ struct Fwd16 {
   static constexpr int SPARE = Dma::kSpare ? 1024 : 0;
   static constexpr int LDS = STAGES * BUF + SPARE;
   static constexpr int OROW = HD * 2 + 16;  // epilogue: row pitch of the 16-bit output tile
-  static_assert(LDS <= 80 * 1024, "two workgroups per CU");
+  static constexpr int WG_PER_CU = HD <= 128 ? 2 : 1;
+  static_assert(LDS <= 160 * 1024 / WG_PER_CU, "LDS budget per workgroup");
   static_assert(4 * 32 * OROW <= LDS, "the output tiles of the four waves fit the staging buffers");
 };
 
 template <class T, int HD>
-__global__ __launch_bounds__(256, 2) void fwd16_kernel(const FwdParams p) {
+__global__ __launch_bounds__(256, (HD <= 128 ? 2 : 1)) void fwd16_kernel(const FwdParams p) {
   typedef Fwd16<HD> C;
   typedef typename C::L L;
   typedef typename Frag<T>::type F;
@@ -253,7 +255,8 @@ static hipError_t fwd_hd(const FwdParams& p, int hd, hipStream_t s, LaunchInfo* 
     case 32: return go16<T, 32>(p, s, info);
     case 64: return go16<T, 64>(p, s, info);
     case 96: return go16<T, 96>(p, s, info);
-    default: return go16<T, 128>(p, s, info);
+    case 128: return go16<T, 128>(p, s, info);
+    default: return go16<T, 256>(p, s, info);
   }
 }
 

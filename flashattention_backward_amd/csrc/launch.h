@@ -69,8 +69,7 @@ struct LaunchInfo {
 };
 
 hipError_t launch_preprocess(const PreParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info);
-// fp32 inputs: launch_fwd, launch_bwd_dkdv, launch_bwd_dq; bf16/fp16: the *16 launchers,
-// except the forward at head dim 256, which takes launch_fwd.
+// fp32 inputs: launch_fwd, launch_bwd_dkdv, launch_bwd_dq; bf16/fp16: the *16 launchers.
 hipError_t launch_fwd(const FwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info);
 hipError_t launch_fwd16(const FwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info);
 hipError_t launch_bwd_dkdv(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info);
