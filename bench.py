@@ -218,6 +218,32 @@ def time_launches(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def per_call_ms(fn, calls):
+    """Milliseconds of each of `calls` calls of fn(), each between its own pair of events
+    recorded on the launch stream (inputs stay resident; caches are not flushed)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def call_stats(ms):
+    """Median, minimum and 90th percentile (linear interpolation) of per-call times."""
+    x = sorted(ms)
+    def pct(q):
+        pos = q * (len(x) - 1)
+        lo = int(pos)
+        hi = min(lo + 1, len(x) - 1)
+        return x[lo] + (x[hi] - x[lo]) * (pos - lo)
+    return {"calls": len(x), "median": round(pct(0.5), 4), "min": round(x[0], 4),
+            "p90": round(pct(0.9), 4)}
+
+
 def bench_workload(w, steps, warmup, with_cpu, inputs=None):
     import torch
     q, k, v, do = inputs if inputs is not None else workloads.make_inputs(w)
@@ -239,6 +265,8 @@ def bench_workload(w, steps, warmup, with_cpu, inputs=None):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     ms = e0.elapsed_time(e1) / steps
+    # the distribution over single calls (a separate loop after the timed region)
+    calls = call_stats(per_call_ms(b.bwd, max(steps, 20)))
     # per-kernel launch times (separate loops, same stream)
     k_ms = {"preprocess": time_launches(b.preprocess, steps, warmup),
             "bwd_dkdv": time_launches(b.dkdv, steps, warmup),
@@ -273,6 +301,8 @@ def bench_workload(w, steps, warmup, with_cpu, inputs=None):
                    "parallelism": "single GPU"},
         "frac_of_peak": round(tflops / peak, 4),
         "wall_ms_per_step": round(wall_ms, 4),
+        "per_call_ms": calls,
+        "caches": "L2 and MALL are not flushed between calls",
         "kernel_ms": {n: round(t, 4) for n, t in k_ms.items()},
         "preprocess_GBps": round(pre_bytes / (k_ms["preprocess"] * 1e-3) / 1e9, 1),
         "forward": {"ms": round(fwd_ms, 4), "tflops": round(fwd_tflops, 2),

@@ -72,3 +72,10 @@ def test_inputs_are_seeded_and_rounded():
     assert all(x.dtype == torch.bfloat16 and x.is_contiguous() for x in a)
     assert all(torch.equal(x, y) for x, y in zip(a, b))
     assert float(a[3].float().std()) < 0.2 < float(a[0].float().std())  # dO scaled by do_std
+
+
+def test_call_stats():
+    s = bench.call_stats([5.0, 1.0, 3.0, 2.0, 4.0])
+    assert s == {"calls": 5, "median": 3.0, "min": 1.0, "p90": 4.6}
+    s = bench.call_stats([float(i) for i in range(1, 21)])  # 1..20
+    assert s["median"] == 10.5 and s["min"] == 1.0 and abs(s["p90"] - 18.1) < 1e-9
