@@ -287,7 +287,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
     constexpr int PER_NB = (PER_CC + KB - 1) / KB;  // ... after each of its MFMAs
     auto pexp = [&](int e) {
       const int nb = e >> 4, r = e & 15;
-      float x = fast_exp2(S[nb][r] * p.scale_log2 - l2[r]);
+      float sv = S[nb][r];
+      order_point(sv);  // not before the MFMA that precedes it in the interleave
+      float x = fast_exp2(sv * p.scale_log2 - l2[r]);
       order_point(x);
       S[nb][r] = x;
       pa[nb][r >> 3][r & 7] = (T)x;
