@@ -199,8 +199,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   // The step is ordered so that the matrix cores always have work while the vector ALU
   // computes the softmax: S first; then dP, with the exponentials of P (which need only S)
   // computed while its MFMAs run; then dV += P^T dO for the first 16 rows while dS of those
-  // rows is formed; dK += dS^T Q for them while dS of the other 16 rows is formed; and last
-  // both products for the second 16 rows.
+  // rows is formed; dK += dS^T Q for them while the last exponentials are formed; dV for the
+  // second 16 rows while their dS is formed; and last dK for the second 16 rows.
   // Operands that open a step: the Q fragments of every head-dim slice and the statistics of
   // this lane's 16 rows (register r of a block holds row m_base + off(r), off(r) = 8 (r / 4) +
   // r % 4).  They are read from the stage of the next step while the current step's last
@@ -279,14 +279,21 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
     // ---- dP = dO V^T, with P = exp2(S scale log2e - lse2) computed in place of S (and its
     // 16-bit copy, the A operand of dV += P^T dO) while the MFMAs run.  Fragment (nb, ks)
-    // holds registers 8 ks .. 8 ks + 7 of block nb.  The dP MFMAs are volatile asm and every
+    // holds registers 8 ks .. 8 ks + 7 of block nb.  The MFMAs are volatile asm and every
     // exponential is pinned between them with order_point(), so the interleave is exact.
+    // A lane's NE exponentials go in the order registers 0..7 of every block (the A operands
+    // of the first dV MFMAs), then registers 8..15.  The dP MFMAs take NE_DP of them, about as
+    // many as their issue time covers (an exponential with its fma and conversion takes about
+    // two thirds of an MFMA's), and never fewer than registers 0..7; the rest run under the
+    // dK MFMAs of rows 0..15, which otherwise leave the vector ALU idle.
     F pa[KB][2], da[KB][2];
-    constexpr int NE = 16 * KB;                  // exponentials of a lane
-    constexpr int PER_CC = (NE + NC - 1) / NC;   // exponentials per head-dim slice
+    constexpr int NE = 16 * KB;
+    constexpr int NE_FIT = NC * KB * 3 / 2;
+    constexpr int NE_DP = NE < NE_FIT ? NE : (NE_FIT > 8 * KB ? NE_FIT : 8 * KB);
+    constexpr int PER_CC = (NE_DP + NC - 1) / NC;   // exponentials per head-dim slice
     constexpr int PER_NB = (PER_CC + KB - 1) / KB;  // ... after each of its MFMAs
     auto pexp = [&](int e) {
-      const int nb = e >> 4, r = e & 15;
+      const int j = e % (8 * KB), nb = j % KB, r = 8 * (e / (8 * KB)) + j / KB;
       float sv = S[nb][r];
       order_point(sv);  // not before the MFMA that precedes it in the interleave
       float x = fast_exp2(sv * p.scale_log2 - l2[r]);
@@ -303,7 +310,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
         else mma_v(dP[nb], ad[cc], bv[nb][cc]);
 #pragma unroll
         for (int k = nb * PER_NB; k < (nb + 1) * PER_NB && k < PER_CC; ++k)
-          if (cc * PER_CC + k < NE) pexp(cc * PER_CC + k);
+          if (cc * PER_CC + k < NE_DP) pexp(cc * PER_CC + k);
       }
     }
     mma_vdrain(dP);
@@ -341,7 +348,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- dK += dS^T Q, rows 0..15, with dS of rows 16..31 formed meanwhile.
+    // ---- dK += dS^T Q, rows 0..15, with the remaining exponentials formed meanwhile.
+    constexpr int NR = NE - NE_DP;
+    constexpr int PER_MMA_E = (NR + NDB * KB - 1) / (NDB * KB);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       bo[db] = b_do(db, 1);
@@ -350,21 +359,27 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
         if (db == 0) mma_a<true>(dk[nb][db], da[nb][0], bq[db]);  // first use of da[nb][0]
         else mma_a(dk[nb][db], da[nb][0], bq[db]);
 #pragma unroll
-        for (int k = 0; k < PER_MMA; ++k) {
-          const int e = (KB * db + nb) * PER_MMA + k;
-          if (e < 8 * KB) ds(e % KB, 8 + e / KB);
+        for (int k = 0; k < PER_MMA_E; ++k) {
+          const int e = (KB * db + nb) * PER_MMA_E + k;
+          if (e < NR) pexp(NE_DP + e);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- dV += P^T dO for rows 16..31, reading the last B operands of this stage.
+    // ---- dV += P^T dO for rows 16..31, reading the last B operands of this stage, with dS of
+    // rows 16..31 formed meanwhile.
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       bq[db] = b_q(db, 1);
 #pragma unroll
       for (int nb = 0; nb < KB; ++nb) {
-        if (db == 0) mma_a<true>(dv[nb][db], pa[nb][1], bo[db]);
+        if (db == 0) mma_a<true>(dv[nb][db], pa[nb][1], bo[db]);  // first use of pa[nb][1]
         else mma_a(dv[nb][db], pa[nb][1], bo[db]);
+#pragma unroll
+        for (int k = 0; k < PER_MMA; ++k) {
+          const int e = (KB * db + nb) * PER_MMA + k;
+          if (e < 8 * KB) ds(e % KB, 8 + e / KB);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
