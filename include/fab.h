@@ -37,6 +37,8 @@
  *
  * Streams: all work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  * the call returns without waiting.  Results are valid for later work on the same stream.
+ * The calls enqueue kernel launches only (no allocation, copy or memset), so they may be
+ * captured into a HIP graph; a replay reads whatever the captured buffers then hold.
  *
  * Errors: every argument is validated before anything is enqueued, so a non-OK status
  * means nothing was launched and no output was written.  fab_last_error() returns a
