@@ -306,8 +306,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
       if (cc + LEAD < NC) read_dp_operands(cc + LEAD);
 #pragma unroll
       for (int nb = 0; nb < KB; ++nb) {
-        if (cc == 0) mma_v0(dP[nb], ad[cc], bv[nb][cc]);
-        else mma_v(dP[nb], ad[cc], bv[nb][cc]);
+        if (cc == 0) mma_v0<false>(dP[nb], ad[cc], bv[nb][cc]);
+        else mma_v<false>(dP[nb], ad[cc], bv[nb][cc]);
 #pragma unroll
         for (int k = nb * PER_NB; k < (nb + 1) * PER_NB && k < PER_CC; ++k)
           if (cc * PER_CC + k < NE_DP) pexp(cc * PER_CC + k);
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
 #pragma unroll
       for (int nb = 0; nb < KB; ++nb) {
         if (db == 0) mma_a<true>(dv[nb][db], pa[nb][0], bo[db]);  // first use of pa[nb][0]
-        else mma_a(dv[nb][db], pa[nb][0], bo[db]);
+        else mma_a<false>(dv[nb][db], pa[nb][0], bo[db]);
 #pragma unroll
         for (int k = 0; k < PER_MMA; ++k) {
           const int e = (KB * db + nb) * PER_MMA + k;  // rows 0..7 of every block
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
 #pragma unroll
       for (int nb = 0; nb < KB; ++nb) {
         if (db == 0) mma_a<true>(dk[nb][db], da[nb][0], bq[db]);  // first use of da[nb][0]
-        else mma_a(dk[nb][db], da[nb][0], bq[db]);
+        else mma_a<false>(dk[nb][db], da[nb][0], bq[db]);
 #pragma unroll
         for (int k = 0; k < PER_MMA_E; ++k) {
           const int e = (KB * db + nb) * PER_MMA_E + k;
@@ -374,7 +374,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
 #pragma unroll
       for (int nb = 0; nb < KB; ++nb) {
         if (db == 0) mma_a<true>(dv[nb][db], pa[nb][1], bo[db]);  // first use of pa[nb][1]
-        else mma_a(dv[nb][db], pa[nb][1], bo[db]);
+        else mma_a<false>(dv[nb][db], pa[nb][1], bo[db]);
 #pragma unroll
         for (int k = 0; k < PER_MMA; ++k) {
           const int e = (KB * db + nb) * PER_MMA + k;
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
 #pragma unroll
       for (int nb = 0; nb < KB; ++nb) {
         if (db == 0) mma_a<true>(dk[nb][db], da[nb][1], bq[db]);
-        else mma_a(dk[nb][db], da[nb][1], bq[db]);
+        else mma_a<false>(dk[nb][db], da[nb][1], bq[db]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -694,7 +694,8 @@ __global__ __launch_bounds__(256, (HD <= 128 ? 2 : 1)) void bwd_dq16_kernel(cons
       for (int db = 0; db < NDB; ++db) {
         F bk_n;
         if (db + 1 < NDB) bk_n = lds_frag_tr<T>(cur, t_off[db + 1][0] + ro, t_off[db + 1][1] + ro);
-        mma_a(dq[db], da[nb][ks], bk);
+        if (db == 0) mma_a<true>(dq[db], da[nb][ks], bk);  // first use of this dS slice
+        else mma_a<false>(dq[db], da[nb][ks], bk);
         if (sl + 1 < 2 * NB) {
 #pragma unroll
           for (int k = 0; k < PER; ++k)

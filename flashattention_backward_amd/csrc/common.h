@@ -51,10 +51,11 @@ __device__ __forceinline__ void mma(f32x16& acc, const f32x8& a, const f32x8& b)
 // between the AGPR and VGPR files; the short-lived score tiles use mma() in VGPRs.
 // Hazards are handled by the caller, because the compiler does not look inside the asm: a
 // VALU write of an A/B operand needs two wait states before the MFMA reads it.  NOP = true
-// (the default) puts them in front (`s_nop 1`).  Dropping them where no producer can be
-// that close was measured slower on gfx950 (the compiler schedules the shorter asm
-// differently), so every asm MFMA keeps them; the build checks the compiled code for this
-// hazard either way (asm_check.py).  Consecutive
+// (the default) puts them in front (`s_nop 1`); callers pass NOP = false where no vector
+// instruction writes the operands (operands read from LDS, or a 16-bit P / dS fragment
+// after its first MFMA).  A lone wave issues about one instruction every five cycles, an
+// s_nop included, so each dropped nop shortens the step.  The build checks the compiled code
+// for this hazard (asm_check.py).  Consecutive
 // MFMAs accumulating into the same registers need no wait states; reads of the
 // accumulators after the last MFMA must go through mma_drain() first.
 template <bool NOP = true>
