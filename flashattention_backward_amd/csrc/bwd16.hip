@@ -8,10 +8,11 @@
 // buffer loads are range-checked: rows past the end of the tensor read as zeros and rows
 // past a head's end read the next head's rows, finite values that the masks and the padding
 // rows' statistics (LSE = +inf, D = 0) neutralise.  (The dK/dV kernel's resident V tile is
-// loaded once with plain loads clamped to the last valid key.)
+// loaded once, with its rows clamped to the last valid key.)
 //
 // Per-row statistics: stats[(b*H + h) * Sq_pad + i] = {LSE * log2(e), D} with
-// Sq_pad = Sq rounded up to 64 (written by the preprocess kernel).
+// Sq_pad = Sq rounded up to 64, written by the preprocess kernel or, on fab_bwd's path, by
+// the dQ kernel's prologue.
 #include <type_traits>
 
 #include "common.h"
