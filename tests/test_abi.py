@@ -137,3 +137,14 @@ def test_probe_library_exports_and_validates():
     assert f(P, 12, 8, 1, 0, None) == 1             # tiles not a multiple of 8
     assert f(P, 64, 8, 1, 4, None) == 1             # no such mode
     assert f(P, 64, 0, 1, 0, None) == 1             # no workgroups
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    """No fallback: with libfab.so absent, every entry point raises instead of computing."""
+    import flashattention_backward_amd as fab
+    monkeypatch.setattr(fab, "_lib", None)
+    monkeypatch.setattr(fab, "LIB_PATH", os.path.join(os.path.dirname(fab.LIB_PATH), "absent", "libfab.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        fab.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        fab.bwd_workspace_bytes(1, 1, 1, 8, 8, 64, 2)
