@@ -22,24 +22,28 @@ namespace fab {
 
 // =======================================================================================
 // dK, dV: key-tile outer (boostr flash_bwd.rs "Step 2": one workgroup per tile of keys).
-// A workgroup owns BN = 128 keys of one (batch, kv head) and walks every query head of the
-// group and every query tile (BM rows) the mask (causal, window) lets reach its keys.  Up to
-// head dim 128 its 4 waves form a 2 x 2 grid: wave (kb, qh) owns keys [64 kb, 64 kb + 64) and
-// the query rows [32 qh, 32 qh + 32) of each 64-row tile, so every Q / dO element read from LDS
-// feeds 64 keys.  At head dim 256 the dK, dV accumulators of 64 keys would not fit, so the grid
-// is 4 x 1: wave kb owns keys [32 kb, 32 kb + 32) and all of a 32-row tile.  A wave's K
+// A workgroup owns BN keys of one (batch, kv head) and walks every query head of the group
+// and every query tile (BM rows) the mask (causal, window) lets reach its keys.  Up to head
+// dim 128 a wave owns 64 keys, so every Q / dO element read from LDS feeds 64 keys: its 4 waves
+// form a 2 x 2 grid over BN = 128 keys (wave (kb, qh) owns keys [64 kb, 64 kb + 64) and the
+// query rows [32 qh, 32 qh + 32) of each 64-row tile), or, in the wide variant, a 4 x 1 grid
+// over BN = 256 keys and 32-row tiles, which halves the number of workgroups and with them the
+// fixed cost of each (the launcher takes it where the grid still gives every CU at least two
+// workgroups).  At head dim 256 the dK, dV accumulators of 64 keys would not fit, so the grid
+// is 4 x 1 with BN = 128: wave kb owns keys [32 kb, 32 kb + 32) and all of a 32-row tile.  A wave's K
 // fragments stay in registers and the V tile in LDS for the workgroup's life (there is no room
 // for V in registers beside the dK, dV accumulators and the score tiles); dK and dV accumulate
 // in AGPRs, and with two query halves they are summed through LDS at the end.
 // =======================================================================================
-template <int HD>
+template <int HD, bool WIDE>
 struct Dkdv16 {
   typedef TileLayout<HD> L;
   // Wave grid: KG groups of keys x QH halves of the query tile.  Up to head dim 128 a wave owns
-  // KB = 2 blocks of 32 keys and half of a 64-row query tile (2 x 2 grid); at 256 its dK, dV
-  // accumulators allow one block, so a wave owns 32 keys and all of a 32-row tile (4 x 1 grid).
-  static constexpr int KB = HD <= 128 ? 2 : 1, QH = KB, KG = 4 / QH;
-  static constexpr int BN = 128, BM = 32 * QH;
+  // KB = 2 blocks of 32 keys and half of a 64-row query tile (2 x 2 grid), or in the wide
+  // variant all of a 32-row tile (4 x 1 grid); at 256 its dK, dV accumulators allow one block,
+  // so a wave owns 32 keys and all of a 32-row tile (4 x 1 grid).
+  static constexpr int KB = HD <= 128 ? 2 : 1, QH = (KB == 2 && !WIDE) ? 2 : 1, KG = 4 / QH;
+  static constexpr int BN = 32 * KB * KG, BM = 32 * QH;
   static constexpr int TILE = L::bytes(BM);    // one Q or dO tile
   static constexpr int STATS = 1024;           // {lse2, D} of 128 rows (one wave-wide load)
   static constexpr int BUF = 2 * TILE + STATS; // one stage: Q, dO, stats
@@ -59,11 +63,11 @@ struct Dkdv16 {
   static_assert(TILE % 16 == 0 && VT % 16 == 0, "granule alignment");
 };
 
-template <class T, int HD>
+template <class T, int HD, bool WIDE>
 __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
-  typedef Dkdv16<HD> C;
+  typedef Dkdv16<HD, WIDE> C;
   typedef typename Frag<T>::type F;
-  typedef TileDma<T, HD, Dkdv16<HD>::BM> Dma;
+  typedef TileDma<T, HD, C::BM> Dma;
   constexpr int NC = HD / 16, NDB = HD / 32;
   static_assert(C::KMAX <= NC, "a tile's prefetch is spread over the head-dim slices");
   constexpr int BM = C::BM, BN = C::BN, KB = C::KB, STAGES = C::STAGES;
@@ -745,14 +749,40 @@ __global__ __launch_bounds__(256, (HD <= 128 ? 2 : 1)) void bwd_dq16_kernel(cons
   }
 }
 
-template <class T, int HD>
-static hipError_t go_dkdv(const BwdParams& p, hipStream_t s, LaunchInfo* info) {
-  typedef Dkdv16<HD> C;
+template <class T, int HD, bool WIDE>
+static hipError_t go_dkdv_cfg(const BwdParams& p, hipStream_t s, LaunchInfo* info) {
+  typedef Dkdv16<HD, WIDE> C;
   const int n_kt = (p.Sk + C::BN - 1) / C::BN;
   const int grid = p.n_units * n_kt;
-  if (info) *info = LaunchInfo{"bwd_dkdv16", grid, 256, C::LDS};
-  hipLaunchKernelGGL((bwd_dkdv16_kernel<T, HD>), dim3(grid), dim3(256), 0, s, p);
+  if (info) *info = LaunchInfo{WIDE ? "bwd_dkdv16_wide" : "bwd_dkdv16", grid, 256, C::LDS};
+  hipLaunchKernelGGL((bwd_dkdv16_kernel<T, HD, WIDE>), dim3(grid), dim3(256), 0, s, p);
   return hipGetLastError();
+}
+
+// Compute units of the current device (queried once per process).
+static int device_cus() {
+  static const int n = [] {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+      (void)hipGetLastError();
+      return 256;
+    }
+    return cus;
+  }();
+  return n;
+}
+
+// The wide (256-key) workgroups halve the per-workgroup fixed cost, but one workgroup per CU
+// leaves the heaviest-first order nothing to balance: they are used only where the grid still
+// gives every CU at least two of them.
+template <class T, int HD>
+static hipError_t go_dkdv(const BwdParams& p, hipStream_t s, LaunchInfo* info) {
+  if constexpr (HD <= 128) {
+    const long long wide_grid = (long long)p.n_units * ((p.Sk + 255) / 256);
+    if (wide_grid >= 2LL * device_cus()) return go_dkdv_cfg<T, HD, true>(p, s, info);
+  }
+  return go_dkdv_cfg<T, HD, false>(p, s, info);
 }
 
 // Key blocks of 32 per step of the dQ kernel (1: 32-key steps through a three-stage ring;
