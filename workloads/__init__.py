@@ -75,8 +75,9 @@ WORKLOADS = {w.name: w for w in [
     Workload("bf16_gqa4_causal_h32_s4096_d128", "bf16", 2, 32, 8, 4096, 4096, 128, True, seed=4),
     Workload("fp16_causal_h16_s16384_d128", "fp16", 1, 16, 16, 16384, 16384, 128, True, seed=51),
     Workload("fp16_gqa4_h16_sq512_sk8192_d128", "fp16", 4, 16, 4, 512, 8192, 128, False, seed=52),
-    # the headline shape at the head dims without a tiled kernel
+    # the headline shape at the other head dims
     Workload("bf16_gqa4_causal_h32_s4096_d32", "bf16", 2, 32, 8, 4096, 4096, 32, True, seed=7),
+    Workload("bf16_gqa4_causal_h32_s4096_d64", "bf16", 2, 32, 8, 4096, 4096, 64, True, seed=10),
     Workload("bf16_gqa4_causal_h32_s4096_d96", "bf16", 2, 32, 8, 4096, 4096, 96, True, seed=8),
     Workload("bf16_gqa4_causal_h32_s4096_d256", "bf16", 2, 32, 8, 4096, 4096, 256, True, seed=9),
     # sliding window of 4096 keys over 16384 positions (a long-context local-attention shape)
