@@ -381,6 +381,40 @@ def atomics_probe(steps, warmup):
             "headline_atomic_dq_ms_at_measured_rate": round(atomic_bytes / rate * 1e3, 3)}
 
 
+def mfma_probe(steps, warmup):
+    """Sustained dense bf16 MFMA throughput of the whole chip and the shader clock it holds
+    meanwhile, from the kernel of libfab_probe.so: every wave issues independent 32x32x16 MFMAs
+    (8 chains) and reads the shader-clock and 100 MHz real-time counters around them."""
+    import numpy as np
+    import torch
+    from flashattention_backward_amd import build as fab_build
+    if not os.path.exists(fab_build.PROBE_LIB):
+        raise RuntimeError(f"{fab_build.PROBE_LIB} is missing: build first")
+    L = ctypes.CDLL(fab_build.PROBE_LIB)
+    L.fab_probe_mfma.restype = ctypes.c_int
+    L.fab_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters, chains = 4 * cus, 4096, 8          # 4 workgroups (16 waves) per CU
+    out = torch.zeros(blocks * 4 * 4, dtype=torch.int64, device="cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for mode, name in enumerate(["same_small_operands", "random_unit_operands"]):
+        def launch():
+            if L.fab_probe_mfma(out.data_ptr(), blocks, iters, mode, stream) != 0:
+                raise RuntimeError("probe launch failed")
+        ms = time_launches(launch, steps, warmup)
+        flops = float(blocks) * 4 * iters * chains * 2 * 32 * 32 * 16
+        tflops = flops / (ms * 1e-3) / 1e12
+        per_wave = out.view(-1, 4).cpu().numpy()
+        clock_mhz = float(np.median(per_wave[:, 0] / per_wave[:, 1])) * 100.0
+        res[name] = {"ms": round(ms, 4), "tflops": round(tflops, 1),
+                     "frac_of_peak": round(tflops / MFMA_PEAK_TFLOPS["bf16"], 4),
+                     "shader_clock_mhz_median": round(clock_mhz, 1),
+                     "flop_per_clk_per_cu": round(tflops * 1e12 / (clock_mhz * 1e6 * cus), 1)}
+    return {"probe": "sustained dense bf16 MFMA throughput (v_mfma_f32_32x32x16_bf16, 8 independent chains per wave)",
+            "cus": cus, "waves": blocks * 4, "mfma_per_wave": iters * chains, "results": res}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -392,6 +426,8 @@ def main():
     ap.add_argument("--only", choices=["bwd", "dkdv", "dq", "preprocess", "fwd", "copy"])
     ap.add_argument("--atomics", action="store_true",
                     help="fp32 atomic-add bandwidth probe (the measurement behind the dQ design)")
+    ap.add_argument("--mfma-peak", action="store_true",
+                    help="sustained MFMA throughput and shader clock of the whole chip")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -401,6 +437,9 @@ def main():
     w = workloads.get(args.workload)
     if args.atomics:
         print(json.dumps(atomics_probe(args.steps, args.warmup)), flush=True)
+        return
+    if args.mfma_peak:
+        print(json.dumps(mfma_probe(args.steps, args.warmup)), flush=True)
         return
     if args.only:
         only_mode(w, args.only, args.steps, args.warmup)

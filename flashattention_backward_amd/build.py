@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfab.so")
 PROBE_LIB = os.path.join(PKG, "libfab_probe.so")
-PROBE_SOURCES = ["probe/atomic_bandwidth.hip"]
+PROBE_SOURCES = ["probe/atomic_bandwidth.hip", "probe/mfma_peak.hip"]
 SOURCES = ["api.hip", "preprocess.hip", "bwd_dkdv.hip", "bwd_dq.hip", "bwd16.hip", "fwd.hip", "fwd16.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -126,8 +126,8 @@ def test_python_binding_rejects_cpu_tensors():
 
 
 def test_probe_library_exports_and_validates():
-    """The atomic-bandwidth probe library (bench.py --atomics) loads, exports its launcher and
-    rejects invalid arguments before touching the GPU."""
+    """The probe library (bench.py --atomics, --mfma-peak) loads, exports its launchers and
+    they reject invalid arguments before touching the GPU."""
     from flashattention_backward_amd import build as fab_build
     L = ctypes.CDLL(fab_build.PROBE_LIB)
     f = L.fab_probe_launch
@@ -137,6 +137,13 @@ def test_probe_library_exports_and_validates():
     assert f(P, 12, 8, 1, 0, None) == 1             # tiles not a multiple of 8
     assert f(P, 64, 8, 1, 4, None) == 1             # no such mode
     assert f(P, 64, 0, 1, 0, None) == 1             # no workgroups
+    g = L.fab_probe_mfma                             # the MFMA-throughput probe (--mfma-peak)
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert g(None, 4, 1, 0, None) == 1               # null output
+    assert g(P, 0, 1, 0, None) == 1                  # no workgroups
+    assert g(P, 4, 0, 0, None) == 1                  # no iterations
+    assert g(P, 4, 1, 2, None) == 1                  # no such mode
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch):
