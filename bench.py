@@ -19,7 +19,6 @@ sample of the same workload, timed on this host's cores before the GPU is touche
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
        python bench.py --only {bwd,dkdv,dq,preprocess,fwd,copy}   (a launch loop for rocprofv3)
-       python bench.py --atomics   (fp32 atomic-add bandwidth probe)
 """
 from __future__ import annotations
 
@@ -95,6 +94,17 @@ def _oracle_group(args):
     return t1 - t0, t2 - t1
 
 
+def blas_build() -> str:
+    """NumPy's BLAS as its build configuration reports it (name, version, configuration)."""
+    import numpy as np
+    try:
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        cfg = blas.get("openblas configuration") or ""
+        return f"{blas.get('name', '?')} {blas.get('version', '?')}" + (f" ({cfg.strip()})" if cfg else "")
+    except Exception as e:  # an older NumPy without dict mode
+        return f"unknown ({type(e).__name__})"
+
+
 def cpu_baseline(w, q, k, v, do, max_groups=None):
     """The fp64 oracle (as it stands) on a bounded sample: whole (batch, kv-head) groups, one
     single-threaded worker process per group, one group per available core.  Runs before the
@@ -113,8 +123,14 @@ def cpu_baseline(w, q, k, v, do, max_groups=None):
                       v[b:b + 1, g:g + 1].double().numpy(), do[b:b + 1, hs].double().numpy(),
                       w.causal, w.scale))
     t0 = time.perf_counter()
-    with mp.get_context("fork").Pool(n) as pool:
+    pool = mp.get_context("fork").Pool(n)
+    try:
         times = pool.map(_oracle_group, tasks)
+    finally:
+        # close + join lets the workers exit on their own; leaving a `with` block would
+        # terminate() them with SIGTERM instead
+        pool.close()
+        pool.join()
     wall = time.perf_counter() - t0
     bwd_wall = max(t[1] for t in times)
     pairs = n * G * w.Sq * w.Sk / (2 if w.causal else 1)
@@ -127,7 +143,8 @@ def cpu_baseline(w, q, k, v, do, max_groups=None):
         "sample": (f"fp64 NumPy oracle backward for {n} of {len(groups)} (batch, kv-head) groups "
                    f"({n * G} of {w.B * w.H} query heads) of {w.name}, one single-threaded "
                    f"process per group; backward wall {bwd_wall:.2f} s (forward, untimed in "
-                   f"value: {max(t[0] for t in times):.2f} s); total {wall:.2f} s"),
+                   f"value: {max(t[0] for t in times):.2f} s); total {wall:.2f} s; NumPy BLAS: "
+                   f"{blas_build()}, one thread per process"),
     }
 
 
@@ -346,75 +363,6 @@ def only_mode(w, what, steps, warmup):
     print(json.dumps({"only": what, "workload": w.name, "launches": warmup + steps}), flush=True)
 
 
-def atomics_probe(steps, warmup):
-    """fp32 atomic-add bandwidth against plain stores and read-modify-writes, in 32 KiB tiles
-    (one 64 x 128 fp32 block of a dQ accumulator), from the kernels of libfab_probe.so; and
-    what the atomic dQ route of the headline workload would cost at the measured rate."""
-    import torch
-    from flashattention_backward_amd import build as fab_build
-    if not os.path.exists(fab_build.PROBE_LIB):
-        raise RuntimeError(f"{fab_build.PROBE_LIB} is missing: build first")
-    L = ctypes.CDLL(fab_build.PROBE_LIB)
-    L.fab_probe_launch.restype = ctypes.c_int
-    L.fab_probe_launch.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 4 + [ctypes.c_void_p]
-    ntiles, blocks, iters, tile = 4096, 1024, 32, 32768   # a 128 MiB buffer
-    buf = torch.zeros(ntiles * tile // 4, dtype=torch.float32, device="cuda:0")
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    payload = blocks * iters * tile
-    names = ["atomic_add_scattered", "atomic_add_xcd_local", "plain_store", "plain_rmw"]
-    res = {}
-    for mode, name in enumerate(names):
-        def launch():
-            if L.fab_probe_launch(buf.data_ptr(), ntiles, blocks, iters, mode, stream) != 0:
-                raise RuntimeError("probe launch failed")
-        ms = time_launches(launch, steps, warmup)
-        res[name] = {"ms": round(ms, 4), "TB_per_s": round(payload / (ms * 1e-3) / 1e12, 3)}
-    w = workloads.get(workloads.HEADLINE)
-    # the atomic route adds one D-wide fp32 row per (key tile of 128, query row it reaches)
-    n_kt = -(-w.Sk // 128)
-    visits = sum(min(n_kt, i // 128 + 1) for i in range(w.Sq)) if w.causal else w.Sq * n_kt
-    atomic_bytes = w.B * w.H * visits * w.D * 4
-    rate = res["atomic_add_scattered"]["TB_per_s"] * 1e12
-    return {"probe": "fp32 atomic add vs plain stores (32 KiB tiles)", "payload_bytes": payload,
-            "blocks": blocks, "iters": iters, "buffer_bytes": ntiles * tile, "results": res,
-            "headline_atomic_dq_bytes": atomic_bytes,
-            "headline_atomic_dq_ms_at_measured_rate": round(atomic_bytes / rate * 1e3, 3)}
-
-
-def mfma_probe(steps, warmup):
-    """Sustained dense bf16 MFMA throughput of the whole chip and the shader clock it holds
-    meanwhile, from the kernel of libfab_probe.so: every wave issues independent 32x32x16 MFMAs
-    (8 chains) and reads the shader-clock and 100 MHz real-time counters around them."""
-    import numpy as np
-    import torch
-    from flashattention_backward_amd import build as fab_build
-    if not os.path.exists(fab_build.PROBE_LIB):
-        raise RuntimeError(f"{fab_build.PROBE_LIB} is missing: build first")
-    L = ctypes.CDLL(fab_build.PROBE_LIB)
-    L.fab_probe_mfma.restype = ctypes.c_int
-    L.fab_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    blocks, iters, chains = 4 * cus, 4096, 8          # 4 workgroups (16 waves) per CU
-    out = torch.zeros(blocks * 4 * 4, dtype=torch.int64, device="cuda:0")
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    res = {}
-    for mode, name in enumerate(["same_small_operands", "random_unit_operands"]):
-        def launch():
-            if L.fab_probe_mfma(out.data_ptr(), blocks, iters, mode, stream) != 0:
-                raise RuntimeError("probe launch failed")
-        ms = time_launches(launch, steps, warmup)
-        flops = float(blocks) * 4 * iters * chains * 2 * 32 * 32 * 16
-        tflops = flops / (ms * 1e-3) / 1e12
-        per_wave = out.view(-1, 4).cpu().numpy()
-        clock_mhz = float(np.median(per_wave[:, 0] / per_wave[:, 1])) * 100.0
-        res[name] = {"ms": round(ms, 4), "tflops": round(tflops, 1),
-                     "frac_of_peak": round(tflops / MFMA_PEAK_TFLOPS["bf16"], 4),
-                     "shader_clock_mhz_median": round(clock_mhz, 1),
-                     "flop_per_clk_per_cu": round(tflops * 1e12 / (clock_mhz * 1e6 * cus), 1)}
-    return {"probe": "sustained dense bf16 MFMA throughput (v_mfma_f32_32x32x16_bf16, 8 independent chains per wave)",
-            "cus": cus, "waves": blocks * 4, "mfma_per_wave": iters * chains, "results": res}
-
-
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -424,10 +372,6 @@ def main():
     ap.add_argument("--all", action="store_true", help="one JSON line per named workload (no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["bwd", "dkdv", "dq", "preprocess", "fwd", "copy"])
-    ap.add_argument("--atomics", action="store_true",
-                    help="fp32 atomic-add bandwidth probe (the measurement behind the dQ design)")
-    ap.add_argument("--mfma-peak", action="store_true",
-                    help="sustained MFMA throughput and shader clock of the whole chip")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -435,12 +379,6 @@ def main():
               f"--gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
     w = workloads.get(args.workload)
-    if args.atomics:
-        print(json.dumps(atomics_probe(args.steps, args.warmup)), flush=True)
-        return
-    if args.mfma_peak:
-        print(json.dumps(mfma_probe(args.steps, args.warmup)), flush=True)
-        return
     if args.only:
         only_mode(w, args.only, args.steps, args.warmup)
         return

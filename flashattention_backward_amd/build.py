@@ -3,9 +3,8 @@
     python -m flashattention_backward_amd.build        # or __graft_entry__.build()
 
 Each .hip source is compiled to an object under ``_build/`` in parallel, then linked into
-``flashattention_backward_amd/libfab.so``.  The measurement kernels of ``csrc/probe/`` (not part
-of the library) are linked on their own into ``libfab_probe.so``.  Always recompiles (the build
-check must exercise the compiler every time).
+``flashattention_backward_amd/libfab.so``.  Always recompiles (the build check must exercise the
+compiler every time).
 """
 from __future__ import annotations
 
@@ -20,8 +19,6 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfab.so")
-PROBE_LIB = os.path.join(PKG, "libfab_probe.so")
-PROBE_SOURCES = ["probe/atomic_bandwidth.hip", "probe/mfma_peak.hip"]
 SOURCES = ["api.hip", "preprocess.hip", "bwd_dkdv.hip", "bwd_dq.hip", "bwd16.hip", "fwd.hip", "fwd16.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -82,13 +79,11 @@ def _link(objs, out: str):
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = SOURCES + PROBE_SOURCES
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    _link(objs[:len(SOURCES)], LIB)
-    _link(objs[len(SOURCES):], PROBE_LIB)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    _link(objs, LIB)
     if verbose:
-        print(f"[fab] built {LIB} and {os.path.basename(PROBE_LIB)}")
+        print(f"[fab] built {LIB}")
     return LIB
 
 

@@ -208,8 +208,12 @@ def grads_for_groups(q, k, v, do, causal: bool, scale: float, groups, jobs: int 
     else:
         import multiprocessing as mp
         ctx = mp.get_context("fork")
-        with ctx.Pool(jobs) as pool:
+        pool = ctx.Pool(jobs)
+        try:
             outs = [r[1] for r in pool.map(_worker, tasks)]
+        finally:
+            pool.close()  # let the workers exit on their own (no SIGTERM from terminate())
+            pool.join()
     res = {}
     for (b, g), out in zip(groups, outs):
         res[(b, g)] = {"o": out["o"][0], "lse": out["lse"][0], "delta": out["delta"][0],

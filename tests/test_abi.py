@@ -125,27 +125,6 @@ def test_python_binding_rejects_cpu_tensors():
         fab.bwd(q, q[0], q, q, q, q[..., 0])
 
 
-def test_probe_library_exports_and_validates():
-    """The probe library (bench.py --atomics, --mfma-peak) loads, exports its launchers and
-    they reject invalid arguments before touching the GPU."""
-    from flashattention_backward_amd import build as fab_build
-    L = ctypes.CDLL(fab_build.PROBE_LIB)
-    f = L.fab_probe_launch
-    f.restype = ctypes.c_int
-    f.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 4 + [ctypes.c_void_p]
-    assert f(None, 64, 8, 1, 0, None) == 1          # null buffer
-    assert f(P, 12, 8, 1, 0, None) == 1             # tiles not a multiple of 8
-    assert f(P, 64, 8, 1, 4, None) == 1             # no such mode
-    assert f(P, 64, 0, 1, 0, None) == 1             # no workgroups
-    g = L.fab_probe_mfma                             # the MFMA-throughput probe (--mfma-peak)
-    g.restype = ctypes.c_int
-    g.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
-    assert g(None, 4, 1, 0, None) == 1               # null output
-    assert g(P, 0, 1, 0, None) == 1                  # no workgroups
-    assert g(P, 4, 0, 0, None) == 1                  # no iterations
-    assert g(P, 4, 1, 2, None) == 1                  # no such mode
-
-
 def test_binding_fails_loudly_without_the_library(monkeypatch):
     """No fallback: with libfab.so absent, every entry point raises instead of computing."""
     import flashattention_backward_amd as fab
