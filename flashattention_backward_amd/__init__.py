@@ -20,7 +20,7 @@ import math
 import os
 import threading
 
-__all__ = ["fwd", "bwd", "bwd_preprocess", "bwd_workspace_bytes", "lib", "FabError",
+__all__ = ["fwd", "bwd", "bwd_noalloc", "bwd_preprocess", "bwd_workspace_bytes", "lib", "FabError",
            "LIB_PATH", "DTYPE_CODES", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfab.so")
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
             L.fab_bwd_preprocess.argtypes = [vp] * 4 + [sz] + [i] * 5 + [vp]
             L.fab_bwd.restype = i
             L.fab_bwd.argtypes = [vp] * 10 + [sz] + [i] * 7 + [i, i, f, vp]
+            L.fab_bwd_noalloc.restype = i
+            L.fab_bwd_noalloc.argtypes = [vp] * 9 + [i] * 7 + [i, i, f, vp]
             L.fab_bwd_dkdv.restype = i
             L.fab_bwd_dkdv.argtypes = [vp] * 5 + [sz] + [vp] * 2 + [i] * 7 + [i, i, f, vp]
             L.fab_bwd_dq.restype = i
@@ -195,4 +197,39 @@ def bwd(do, q, k, v, o, lse, num_heads: int | None = None, num_kv_heads: int | N
                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                          B, H, H_kv, Sq, Sk, D, code, int(bool(causal)), _window(window_size),
                          float(scale), _stream_handle(dev)))
+    return dq, dk, dv
+
+
+def bwd_noalloc(do, q, k, v, o, lse, causal: bool = False, scale: float | None = None,
+                window_size: int = 0, out=None):
+    """The backward through fab_bwd_noalloc: no workspace; the library keeps the per-row
+    statistics in its static per-GPU scratch (at most 2^21 padded query rows, B * H * Sq
+    rounded up to 64).  ``out`` = (dq, dk, dv) preallocated tensors to write into (so that the
+    call itself allocates nothing); by default they are allocated here.  Calls that overlap on
+    one GPU race on the shared scratch."""
+    import torch
+    _require(q.dim() == 4, "q", f"must be 4-D [B, H, Sq, D], got {tuple(q.shape)}")
+    _require(k.dim() == 4, "k", f"must be 4-D [B, H_kv, Sk, D], got {tuple(k.shape)}")
+    B, H, Sq, D = q.shape
+    H_kv, Sk = k.shape[1], k.shape[2]
+    dev, dt = q.device, q.dtype
+    _check_tensor(q, "q", (B, H, Sq, D), dt, dev)
+    _check_tensor(k, "k", (B, H_kv, Sk, D), dt, dev)
+    _check_tensor(v, "v", (B, H_kv, Sk, D), dt, dev)
+    _check_tensor(o, "output", (B, H, Sq, D), dt, dev)
+    _check_tensor(do, "dout", (B, H, Sq, D), dt, dev)
+    _check_tensor(lse, "lse", (B, H, Sq), torch.float32, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = out
+    _check_tensor(dq, "dq", (B, H, Sq, D), dt, dev)
+    _check_tensor(dk, "dk", (B, H_kv, Sk, D), dt, dev)
+    _check_tensor(dv, "dv", (B, H_kv, Sk, D), dt, dev)
+    _check(lib().fab_bwd_noalloc(do.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                 o.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                 dv.data_ptr(), B, H, H_kv, Sq, Sk, D, _dtype_code(q),
+                                 int(bool(causal)), _window(window_size), float(scale),
+                                 _stream_handle(dev)))
     return dq, dk, dv

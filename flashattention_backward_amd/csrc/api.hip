@@ -12,10 +12,19 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/fab.h"
 #include "launch.h"
+
+// Static scratch of fab_bwd_noalloc, for callers that cannot allocate device memory: it holds
+// the per-row statistics {lse * log2(e), D} that fab_bwd keeps in its workspace.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device copy: host code uses only the address that
+// hipGetSymbolAddress returns for the current device (scratch_device_ptr below).
+constexpr size_t kScratchBytes = size_t(16) << 20;  // 2^21 padded query rows of 8 bytes
+static __device__ __align__(256) char scratch[kScratchBytes];
 
 namespace {
 
@@ -221,6 +230,58 @@ fab_status launched(hipError_t e, const char* what) {
   return FAB_OK;
 }
 
+// Device address of the current device's copy of `scratch`, looked up once per device (with
+// that device current) and kept for the life of the process.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+fab_status scratch_device_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FAB_ERR_DEVICE, "scratch", "no usable GPU (%s)", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FAB_ERR_DEVICE, "scratch", "device index %d beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return fail(FAB_ERR_DEVICE, "scratch", "hipGetSymbolAddress failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FAB_OK;
+}
+
+// The launches of the backward, after validation.  `workspace` holds the per-row statistics.
+fab_status run_bwd(const void* dO, const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                   int B, int H, int H_kv, int Sq, int Sk, int D, int dtype, int causal,
+                   int window_size, float scale, hipStream_t s) {
+  fab::LaunchInfo li;
+  const fab::BwdParams p =
+      bwd_params(dO, q, k, v, workspace, dq, dk, dv, B, H, H_kv, Sq, Sk, causal, window_size, scale);
+  if (tiled(dtype)) {
+    // Step 1 runs inside the dQ kernel, which therefore goes first: it writes the row
+    // statistics the dK/dV kernel then reads from the workspace.
+    fab::BwdParams pq = p;
+    pq.o = o; pq.lse = lse; pq.stats_out = static_cast<float*>(workspace);
+    FAB_TRY(launched(fab::launch_bwd_dq16(pq, dtype, D, s, &li), "bwd_dq"));
+    log_launch(li);
+    FAB_TRY(launched(launch_step2(p, dtype, D, s, true, false, &li), "bwd_dkdv"));
+    return FAB_OK;
+  }
+  const fab::PreParams pp = pre_params(dO, o, lse, workspace, B, H, Sq);
+  FAB_TRY(launched(fab::launch_preprocess(pp, dtype, D, s, &li), "preprocess"));
+  log_launch(li);
+  FAB_TRY(launched(launch_step2(p, dtype, D, s, true, true, &li), "step 2"));
+  return FAB_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -315,25 +376,38 @@ fab_status fab_bwd(const void* dO, const void* q, const void* k, const void* v,
   FAB_TRY(check_device_range(dv, nk, "dv"));
   FAB_TRY(check_device_range(workspace, ws_bytes(B, H, Sq), "workspace"));
 
-  hipStream_t s = (hipStream_t)stream;
-  fab::LaunchInfo li;
-  const fab::BwdParams p =
-      bwd_params(dO, q, k, v, workspace, dq, dk, dv, B, H, H_kv, Sq, Sk, causal, window_size, scale);
-  if (tiled(dtype)) {
-    // Step 1 runs inside the dQ kernel, which therefore goes first: it writes the row
-    // statistics the dK/dV kernel then reads from the workspace.
-    fab::BwdParams pq = p;
-    pq.o = o; pq.lse = lse; pq.stats_out = static_cast<float*>(workspace);
-    FAB_TRY(launched(fab::launch_bwd_dq16(pq, dtype, D, s, &li), "bwd_dq"));
-    log_launch(li);
-    FAB_TRY(launched(launch_step2(p, dtype, D, s, true, false, &li), "bwd_dkdv"));
-    return FAB_OK;
-  }
-  const fab::PreParams pp = pre_params(dO, o, lse, workspace, B, H, Sq);
-  FAB_TRY(launched(fab::launch_preprocess(pp, dtype, D, s, &li), "preprocess"));
-  log_launch(li);
-  FAB_TRY(launched(launch_step2(p, dtype, D, s, true, true, &li), "step 2"));
-  return FAB_OK;
+  return run_bwd(dO, q, k, v, o, lse, dq, dk, dv, workspace, B, H, H_kv, Sq, Sk, D, dtype, causal,
+                 window_size, scale, (hipStream_t)stream);
+}
+
+fab_status fab_bwd_noalloc(const void* dO, const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, void* dq, void* dk, void* dv,
+                           int B, int H, int H_kv, int Sq, int Sk, int D, int dtype,
+                           int causal, int window_size, float scale, void* stream) {
+  FAB_TRY(check_bwd_inputs(dO, q, k, v, B, H, H_kv, Sq, Sk, D, dtype, window_size, scale));
+  FAB_TRY(check_ptr(o, "o"));
+  FAB_TRY(check_ptr(lse, "lse"));
+  FAB_TRY(check_ptr(dq, "dq"));
+  FAB_TRY(check_ptr(dk, "dk"));
+  FAB_TRY(check_ptr(dv, "dv"));
+  const size_t need = ws_bytes(B, H, Sq);
+  if (need > kScratchBytes)
+    return fail(FAB_ERR_INVALID_ARGUMENT, "dims",
+                "needs %zu bytes of statistics (B * num_heads * Sq rounded up to 64 = %lld rows), "
+                "the static scratch holds %zu (%zu rows)", need,
+                (long long)B * H * fab::stats_rows(Sq), kScratchBytes, kScratchBytes / 8);
+  const size_t es = elem_size(dtype);
+  const size_t nq = (size_t)B * H * Sq * D * es, nk = (size_t)B * H_kv * Sk * D * es;
+  FAB_TRY(check_bwd_device(dO, q, k, v, B, H, H_kv, Sq, Sk, D, dtype));
+  FAB_TRY(check_device_range(o, nq, "o"));
+  FAB_TRY(check_device_range(lse, (size_t)B * H * Sq * 4, "lse"));
+  FAB_TRY(check_device_range(dq, nq, "dq"));
+  FAB_TRY(check_device_range(dk, nk, "dk"));
+  FAB_TRY(check_device_range(dv, nk, "dv"));
+  void* ws = nullptr;
+  FAB_TRY(scratch_device_ptr(&ws));
+  return run_bwd(dO, q, k, v, o, lse, dq, dk, dv, ws, B, H, H_kv, Sq, Sk, D, dtype, causal,
+                 window_size, scale, (hipStream_t)stream);
 }
 
 fab_status fab_bwd_dkdv(const void* dO, const void* q, const void* k, const void* v,

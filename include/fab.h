@@ -4,7 +4,8 @@
  * C ABI.  Every tensor argument is a plain device pointer to dense, row-major memory; no
  * PyTorch (or any other framework) type appears here.  The caller owns and allocates all
  * memory, including the backward workspace; the library never allocates or frees device
- * memory and keeps no pointer after a call returns.
+ * memory and keeps no pointer after a call returns.  (The one exception is the static scratch
+ * array of fab_bwd_noalloc, loaded with the library's code on each GPU it runs on.)
  *
  * Operation (boostr 0.1.0, src/ops/cuda/attention/flash_bwd.rs, doc comment of
  * flash_attention_bwd_impl): the backward runs in two steps -- a preprocessing step that
@@ -127,6 +128,24 @@ fab_status fab_bwd(const void* dO, const void* q, const void* k, const void* v,
                    void* workspace, size_t workspace_bytes,
                    int B, int num_heads, int num_kv_heads, int Sq, int Sk, int D, int dtype,
                    int causal, int window_size, float scale, void* stream);
+
+/*
+ * fab_bwd without a workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  It computes
+ * what fab_bwd computes, with the same kernels, and calls no allocating routine: the per-row
+ * statistics that fab_bwd keeps in its workspace go to a static scratch array of the library,
+ * 16 MiB per GPU, held from the first call on a device until the process ends.  Limit:
+ * B * num_heads * (Sq rounded up to 64) <= 2^21 rows; larger sizes return
+ * FAB_ERR_INVALID_ARGUMENT before anything is launched.  Every call on one GPU shares that
+ * GPU's scratch: calls that may overlap on one GPU (different streams without ordering, or
+ * different threads) race and give undefined results; calls ordered on one stream are safe.
+ * The scratch needs no initialisation (each call writes every entry it reads).  Other
+ * arguments, outputs and errors as for fab_bwd.
+ */
+fab_status fab_bwd_noalloc(const void* dO, const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, void* dq, void* dk, void* dv,
+                           int B, int num_heads, int num_kv_heads, int Sq, int Sk, int D, int dtype,
+                           int causal, int window_size, float scale, void* stream);
 
 /*
  * The two kernels of step 2 on their own, for inspection and per-kernel timing; fab_bwd

@@ -116,6 +116,35 @@ def test_error_message_is_thread_local():
     assert "dtype" in L.fab_last_error().decode()
 
 
+def bwd_noalloc(**kw):
+    a = dict(dO=P, q=P, k=P, v=P, o=P, lse=P, dq=P, dk=P, dv=P,
+             B=1, H=4, H_kv=2, Sq=16, Sk=16, D=64, dtype=2, causal=1, window=0, scale=0.125)
+    a.update(kw)
+    L = fab.lib()
+    st = L.fab_bwd_noalloc(a["dO"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["dq"], a["dk"],
+                           a["dv"], a["B"], a["H"], a["H_kv"], a["Sq"], a["Sk"], a["D"], a["dtype"],
+                           a["causal"], a["window"], a["scale"], None)
+    return st, L.fab_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    # 2^21 + 64 padded rows of statistics: one row group past the static scratch
+    (dict(B=1, H=1, H_kv=1, Sq=(1 << 21) + 1, Sk=16, D=64), 1, "static scratch"),
+    (dict(B=33, H=64, H_kv=8, Sq=1000, Sk=1000, D=128), 1, "static scratch"),
+    (dict(dtype=3), 2, "dtype"),
+    (dict(H=3), 1, "num_kv_heads"),
+    (dict(dq=0), 1, "dq: null"),
+    (dict(o=P + 4), 1, "o: pointer"),
+    (dict(scale=float("nan")), 1, "scale"),
+])
+def test_bwd_noalloc_rejects_invalid_arguments(kw, status, needle):
+    """The no-allocation entry point validates before touching the GPU, including its limit:
+    B * num_heads * (Sq rounded up to 64) <= 2^21 rows of statistics."""
+    st, msg = bwd_noalloc(**kw)
+    assert st == status, (st, msg)
+    assert needle in msg, msg
+
+
 def test_python_binding_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     q = torch.zeros(1, 2, 8, 64)
