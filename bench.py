@@ -43,8 +43,12 @@ HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "flashattention_backward_amd", "csrc")
 
-# Contractions each kernel performs per allowed (b, h, query, key) pair, in units of 2*D FLOPs.
-KERNEL_CONTRACTIONS = {"bwd_dkdv": 4, "bwd_dq": 3}
+# Contractions each kernel performs per allowed (b, h, query, key) pair, in units of 2*D FLOPs:
+# the dK/dV kernel forms S, dP, dV and dK; the dQ kernel dQ alone from stored dS, or S, dP and
+# dQ where it recomputes dS.
+KERNEL_CONTRACTIONS = {"stored_ds": {"bwd_dkdv": 4, "bwd_dq": 1},
+                       "recompute": {"bwd_dkdv": 4, "bwd_dq": 3}}
+MODES = ("stored_ds", "recompute")
 KERNEL_SOURCE = {"bwd_dkdv": "bwd16.hip", "bwd_dq": "bwd16.hip", "preprocess": "preprocess.hip"}
 
 
@@ -152,7 +156,7 @@ def cpu_baseline(w, q, k, v, do, max_groups=None):
 class Bwd:
     """Preallocated buffers and raw C-ABI calls for one workload (no allocation per step)."""
 
-    def __init__(self, w, q, k, v, do):
+    def __init__(self, w, q, k, v, do, mode="stored_ds"):
         import torch
 
         import flashattention_backward_amd as fab
@@ -165,7 +169,12 @@ class Bwd:
         self.dk = torch.empty_like(self.k)
         self.dv = torch.empty_like(self.v)
         self.code = fab.DTYPE_CODES[str(self.q.dtype).replace("torch.", "")]
-        nb = fab.bwd_workspace_bytes(w.B, w.H, w.H_kv, w.Sq, w.Sk, w.D, self.code)
+        # the workspace size selects the mode; the stored-dS size falls back to the recompute
+        # size where that mode does not apply (float32, very large dS buffers)
+        nb = fab.bwd_workspace_bytes(w.B, w.H, w.H_kv, w.Sq, w.Sk, w.D, self.code,
+                                     store_ds=(mode == "stored_ds"))
+        nmin = fab.bwd_workspace_bytes(w.B, w.H, w.H_kv, w.Sq, w.Sk, w.D, self.code, store_ds=False)
+        self.mode = "stored_ds" if nb > nmin else "recompute"
         self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
         self.stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         self.dims = (w.B, w.H, w.H_kv, w.Sq, w.Sk, w.D, self.code, int(w.causal), w.window,
@@ -261,11 +270,11 @@ def call_stats(ms):
             "p90": round(pct(0.9), 4)}
 
 
-def bench_workload(w, steps, warmup, with_cpu, inputs=None):
+def bench_workload(w, steps, warmup, with_cpu, inputs=None, mode="stored_ds"):
     import torch
     q, k, v, do = inputs if inputs is not None else workloads.make_inputs(w)
     cpu = cpu_baseline(w, q, k, v, do) if with_cpu else None
-    b = Bwd(w, q, k, v, do)
+    b = Bwd(w, q, k, v, do, mode=mode)
     torch.cuda.synchronize()
     settle(b.bwd)
     # the timed region: `steps` whole backward calls, synchronised on both sides
@@ -284,7 +293,8 @@ def bench_workload(w, steps, warmup, with_cpu, inputs=None):
     ms = e0.elapsed_time(e1) / steps
     # the distribution over single calls (a separate loop after the timed region)
     calls = call_stats(per_call_ms(b.bwd, max(steps, 20)))
-    # per-kernel launch times (separate loops, same stream)
+    # per-kernel launch times (separate loops, same stream; in the stored-dS mode the dQ loop
+    # reads the dS that the dK/dV loop stored)
     k_ms = {"preprocess": time_launches(b.preprocess, steps, warmup),
             "bwd_dkdv": time_launches(b.dkdv, steps, warmup),
             "bwd_dq": time_launches(b.dq_, steps, warmup)}
@@ -296,7 +306,7 @@ def bench_workload(w, steps, warmup, with_cpu, inputs=None):
     tflops = flops / (ms * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[w.dtype]
     dom = max(("bwd_dkdv", "bwd_dq"), key=lambda n: k_ms[n])
-    kflops = 2.0 * w.D * KERNEL_CONTRACTIONS[dom] * allowed_pairs(w)
+    kflops = 2.0 * w.D * KERNEL_CONTRACTIONS[b.mode][dom] * allowed_pairs(w)
     achieved = kflops / (k_ms[dom] * 1e-3) / 1e12
     es = 4 if w.dtype == "fp32" else 2
     pre_bytes = w.B * w.H * w.Sq * (2 * w.D * es + 4 + 8)  # read dO, O, LSE; write {LSE', D}
@@ -317,6 +327,8 @@ def bench_workload(w, steps, warmup, with_cpu, inputs=None):
                    "D": w.D, "causal": w.causal, "scale": w.scale, "seed": w.seed,
                    "parallelism": "single GPU"},
         "frac_of_peak": round(tflops / peak, 4),
+        "mode": b.mode,
+        "workspace_bytes": int(b.ws.numel()),
         "wall_ms_per_step": round(wall_ms, 4),
         "per_call_ms": calls,
         "caches": "L2 and MALL are not flushed between calls",
@@ -339,7 +351,7 @@ def bench_workload(w, steps, warmup, with_cpu, inputs=None):
     return line
 
 
-def only_mode(w, what, steps, warmup):
+def only_mode(w, what, steps, warmup, mode="stored_ds"):
     """A bare launch loop for rocprofv3 (no timing, no CPU baseline)."""
     import torch
     if what == "copy":
@@ -353,10 +365,12 @@ def only_mode(w, what, steps, warmup):
         print(json.dumps({"only": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
                           "launches": warmup + steps}), flush=True)
         return
-    b = Bwd(w, *workloads.make_inputs(w))
+    b = Bwd(w, *workloads.make_inputs(w), mode=mode)
     fn = {"bwd": b.bwd, "dkdv": b.dkdv, "dq": b.dq_, "preprocess": b.preprocess, "fwd": b.fwd}[what]
     if what in ("dkdv", "dq"):
         b.preprocess()
+    if what == "dq":
+        b.dkdv()  # the stored-dS dQ kernel reads what the dK/dV kernel stores
     for _ in range(warmup + steps):
         fn()
     torch.cuda.synchronize()
@@ -372,6 +386,9 @@ def main():
     ap.add_argument("--all", action="store_true", help="one JSON line per named workload (no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["bwd", "dkdv", "dq", "preprocess", "fwd", "copy"])
+    ap.add_argument("--mode", choices=MODES, default="stored_ds",
+                    help="how dQ is formed: from the dS the dK/dV kernel stores (default, where it "
+                         "applies) or by recomputing S and dP")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -380,13 +397,14 @@ def main():
         sys.exit(2)
     w = workloads.get(args.workload)
     if args.only:
-        only_mode(w, args.only, args.steps, args.warmup)
+        only_mode(w, args.only, args.steps, args.warmup, args.mode)
         return
     if args.all:
         for name in workloads.WORKLOADS:
-            print(json.dumps(bench_workload(workloads.get(name), args.steps, args.warmup, False)), flush=True)
+            print(json.dumps(bench_workload(workloads.get(name), args.steps, args.warmup, False,
+                                            mode=args.mode)), flush=True)
         return
-    line = bench_workload(w, args.steps, args.warmup, not args.no_cpu_baseline)
+    line = bench_workload(w, args.steps, args.warmup, not args.no_cpu_baseline, mode=args.mode)
     print(json.dumps(line), flush=True)
 
 

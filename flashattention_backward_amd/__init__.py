@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
             L.fab_last_error.restype = ctypes.c_char_p
             L.fab_bwd_workspace_bytes.restype = sz
             L.fab_bwd_workspace_bytes.argtypes = [i] * 7
+            L.fab_bwd_workspace_bytes_min.restype = sz
+            L.fab_bwd_workspace_bytes_min.argtypes = [i] * 7
             L.fab_fwd.restype = i
             L.fab_fwd.argtypes = [vp] * 5 + [i] * 7 + [i, i, f, vp]
             L.fab_bwd_preprocess.restype = i
@@ -103,8 +105,11 @@ def _check_tensor(t, name, shape, dtype, device):
     _require(t.is_contiguous(), name, "must be contiguous")
 
 
-def bwd_workspace_bytes(B, H, H_kv, Sq, Sk, D, dtype_code) -> int:
-    return int(lib().fab_bwd_workspace_bytes(B, H, H_kv, Sq, Sk, D, dtype_code))
+def bwd_workspace_bytes(B, H, H_kv, Sq, Sk, D, dtype_code, store_ds: bool = True) -> int:
+    """Workspace bytes for the fastest mode (store_ds=True: stored dS where it applies) or the
+    least fab_bwd accepts (store_ds=False: dQ recomputes dS)."""
+    f = lib().fab_bwd_workspace_bytes if store_ds else lib().fab_bwd_workspace_bytes_min
+    return int(f(B, H, H_kv, Sq, Sk, D, dtype_code))
 
 
 def _window(window_size) -> int:
@@ -161,9 +166,12 @@ def bwd_preprocess(do, o, lse):
 
 
 def bwd(do, q, k, v, o, lse, num_heads: int | None = None, num_kv_heads: int | None = None,
-        causal: bool = False, scale: float | None = None, workspace=None, window_size: int = 0):
+        causal: bool = False, scale: float | None = None, workspace=None, window_size: int = 0,
+        store_ds: bool = True):
     """The backward: returns (dq, dk, dv) with the shapes and dtype of (q, k, v).  `causal`,
-    `scale` and `window_size` must be those the forward ran with."""
+    `scale` and `window_size` must be those the forward ran with.  Without a `workspace`, one is
+    allocated for the stored-dS mode (store_ds=True, where it applies) or for the recompute
+    mode (store_ds=False); a given workspace selects the mode by its size."""
     import torch
     _require(q.dim() == 4, "q", f"must be 4-D [B, H, Sq, D], got {tuple(q.shape)}")
     _require(k.dim() == 4, "k", f"must be 4-D [B, H_kv, Sk, D], got {tuple(k.shape)}")
@@ -184,9 +192,10 @@ def bwd(do, q, k, v, o, lse, num_heads: int | None = None, num_kv_heads: int | N
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     code = _dtype_code(q)
-    need = bwd_workspace_bytes(B, H, H_kv, Sq, Sk, D, code)
+    need = bwd_workspace_bytes(B, H, H_kv, Sq, Sk, D, code, store_ds=False)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        nb = bwd_workspace_bytes(B, H, H_kv, Sq, Sk, D, code, store_ds=store_ds)
+        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
     _require(workspace.is_cuda and workspace.numel() * workspace.element_size() >= need,
              "workspace", f"needs {need} bytes on {dev}")
     dq = torch.empty_like(q)

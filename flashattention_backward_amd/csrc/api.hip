@@ -125,9 +125,40 @@ fab_status check_device_range(const void* p, size_t bytes, const char* name) {
   return FAB_OK;
 }
 
+// Workspace: the per-row statistics, B * H * Sq_pad float pairs, rounded up to 256 bytes.
 size_t ws_bytes(long long B, long long H, long long Sq) {
   const size_t d = (size_t)(B * H) * fab::stats_rows((int)Sq) * 8;
   return (d + 255) / 256 * 256;
+}
+
+// Stored-dS mode (16-bit inputs): the workspace also holds every dS fragment the dK/dV kernel
+// forms, one slab of ds_rows(Sq) x ds_keys(Sk) 16-bit values per (b, h), from a 4 KB
+// boundary after the statistics.  The kernels address a slab with 32-bit offsets (a group's G
+// slabs with one buffer resource), and the whole buffer is capped so that the mode stays a
+// choice for sizes where memory is plentiful; beyond, dQ recomputes dS.
+constexpr unsigned long long kDsMaxBytes = 32ULL << 30;
+
+unsigned long long ds_slab_bytes(int Sq, int Sk) {
+  return (unsigned long long)fab::ds_rows(Sq) * (unsigned long long)fab::ds_keys(Sk) * 2ULL;
+}
+
+bool ds_mode_fits(int B, int H, int H_kv, int Sq, int Sk, int dtype) {
+  if (dtype == FAB_F32) return false;
+  const unsigned long long slab = ds_slab_bytes(Sq, Sk);
+  return slab <= (1ULL << 31) && (unsigned long long)(H / H_kv) * slab < (1ULL << 32) &&
+         (unsigned long long)B * H * slab <= kDsMaxBytes;
+}
+
+size_t ds_offset(int B, int H, int Sq) { return (ws_bytes(B, H, Sq) + 4095) / 4096 * 4096; }
+
+size_t ws_bytes_ds(int B, int H, int Sq, int Sk) {
+  return ds_offset(B, H, Sq) + (size_t)B * H * ds_slab_bytes(Sq, Sk);
+}
+
+// The workspace selects the mode: with at least ws_bytes_ds (and sizes the mode takes) the
+// dK/dV kernel stores dS and dQ reads it back; with less (at least ws_bytes) dQ recomputes it.
+bool use_ds(size_t given, int B, int H, int H_kv, int Sq, int Sk, int dtype) {
+  return ds_mode_fits(B, H, H_kv, Sq, Sk, dtype) && given >= ws_bytes_ds(B, H, Sq, Sk);
 }
 
 int units_per_xcd(int n_units) { return n_units % 8 == 0 ? n_units / 8 : 0; }
@@ -152,6 +183,7 @@ fab::BwdParams bwd_params(const void* dO, const void* q, const void* k, const vo
   p.q = q; p.k = k; p.v = v; p.dO = dO; p.stats = static_cast<const float*>(workspace);
   p.dq = dq; p.dk = dk; p.dv = dv;
   p.o = nullptr; p.lse = nullptr; p.stats_out = nullptr;
+  p.ds = nullptr; p.ds_slab = 0; p.ds_nk32 = 0;
   p.B = B; p.H = H; p.H_kv = H_kv; p.Sq = Sq; p.Sk = Sk; p.Sq_pad = fab::stats_rows(Sq);
   p.causal = causal ? 1 : 0;
   p.win = kernel_window(window_size, Sq, Sk);
@@ -167,6 +199,13 @@ fab::BwdParams bwd_params(const void* dO, const void* q, const void* k, const vo
   p.n_units = B * H_kv;
   p.units_per_xcd = units_per_xcd(p.n_units);
   return p;
+}
+
+// The dK/dV kernel writes the dS region, the dQ kernel only reads it.
+void set_ds(fab::BwdParams& p, const void* workspace) {
+  p.ds = const_cast<char*>(static_cast<const char*>(workspace)) + ds_offset(p.B, p.H, p.Sq);
+  p.ds_slab = (unsigned)ds_slab_bytes(p.Sq, p.Sk);
+  p.ds_nk32 = (int)(fab::ds_keys(p.Sk) / 32);
 }
 
 // Checks shared by fab_bwd and the two step-2 entry points (every pointer but dq/dk/dv).
@@ -259,12 +298,23 @@ fab_status scratch_device_ptr(void** out) {
 
 // The launches of the backward, after validation.  `workspace` holds the per-row statistics.
 fab_status run_bwd(const void* dO, const void* q, const void* k, const void* v, const void* o,
-                   const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                   const float* lse, void* dq, void* dk, void* dv, void* workspace, bool ds,
                    int B, int H, int H_kv, int Sq, int Sk, int D, int dtype, int causal,
                    int window_size, float scale, hipStream_t s) {
   fab::LaunchInfo li;
-  const fab::BwdParams p =
+  fab::BwdParams p =
       bwd_params(dO, q, k, v, workspace, dq, dk, dv, B, H, H_kv, Sq, Sk, causal, window_size, scale);
+  if (ds) {
+    // Stored dS: step 1, then the dK/dV kernel (which also writes dS), then dQ = scale dS K.
+    set_ds(p, workspace);
+    const fab::PreParams pp = pre_params(dO, o, lse, workspace, B, H, Sq);
+    FAB_TRY(launched(fab::launch_preprocess(pp, dtype, D, s, &li), "preprocess"));
+    log_launch(li);
+    FAB_TRY(launched(launch_step2(p, dtype, D, s, true, false, &li), "bwd_dkdv"));
+    FAB_TRY(launched(fab::launch_bwd_dq_ds16(p, dtype, D, s, &li), "bwd_dq"));
+    log_launch(li);
+    return FAB_OK;
+  }
   if (tiled(dtype)) {
     // Step 1 runs inside the dQ kernel, which therefore goes first: it writes the row
     // statistics the dK/dV kernel then reads from the workspace.
@@ -291,6 +341,14 @@ const char* fab_version(void) { return "fab 0.1.0 (gfx950)"; }
 const char* fab_last_error(void) { return g_last_error.c_str(); }
 
 size_t fab_bwd_workspace_bytes(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype) {
+  std::string saved = g_last_error;
+  fab_status s = check_common(B, H, H_kv, Sq, Sk, D, dtype);
+  g_last_error = saved;
+  if (s != FAB_OK) return 0;
+  return ds_mode_fits(B, H, H_kv, Sq, Sk, dtype) ? ws_bytes_ds(B, H, Sq, Sk) : ws_bytes(B, H, Sq);
+}
+
+size_t fab_bwd_workspace_bytes_min(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype) {
   std::string saved = g_last_error;
   fab_status s = check_common(B, H, H_kv, Sq, Sk, D, dtype);
   g_last_error = saved;
@@ -374,10 +432,11 @@ fab_status fab_bwd(const void* dO, const void* q, const void* k, const void* v,
   FAB_TRY(check_device_range(dq, nq, "dq"));
   FAB_TRY(check_device_range(dk, nk, "dk"));
   FAB_TRY(check_device_range(dv, nk, "dv"));
-  FAB_TRY(check_device_range(workspace, ws_bytes(B, H, Sq), "workspace"));
+  const bool ds = use_ds(workspace_bytes, B, H, H_kv, Sq, Sk, dtype);
+  FAB_TRY(check_device_range(workspace, ds ? ws_bytes_ds(B, H, Sq, Sk) : ws_bytes(B, H, Sq), "workspace"));
 
-  return run_bwd(dO, q, k, v, o, lse, dq, dk, dv, workspace, B, H, H_kv, Sq, Sk, D, dtype, causal,
-                 window_size, scale, (hipStream_t)stream);
+  return run_bwd(dO, q, k, v, o, lse, dq, dk, dv, workspace, ds, B, H, H_kv, Sq, Sk, D, dtype,
+                 causal, window_size, scale, (hipStream_t)stream);
 }
 
 fab_status fab_bwd_noalloc(const void* dO, const void* q, const void* k, const void* v,
@@ -406,12 +465,12 @@ fab_status fab_bwd_noalloc(const void* dO, const void* q, const void* k, const v
   FAB_TRY(check_device_range(dv, nk, "dv"));
   void* ws = nullptr;
   FAB_TRY(scratch_device_ptr(&ws));
-  return run_bwd(dO, q, k, v, o, lse, dq, dk, dv, ws, B, H, H_kv, Sq, Sk, D, dtype, causal,
+  return run_bwd(dO, q, k, v, o, lse, dq, dk, dv, ws, false, B, H, H_kv, Sq, Sk, D, dtype, causal,
                  window_size, scale, (hipStream_t)stream);
 }
 
 fab_status fab_bwd_dkdv(const void* dO, const void* q, const void* k, const void* v,
-                        const void* workspace, size_t workspace_bytes, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, void* dk, void* dv,
                         int B, int H, int H_kv, int Sq, int Sk, int D,
                         int dtype, int causal, int window_size, float scale, void* stream) {
   FAB_TRY(check_bwd_inputs(dO, q, k, v, B, H, H_kv, Sq, Sk, D, dtype, window_size, scale));
@@ -420,11 +479,13 @@ fab_status fab_bwd_dkdv(const void* dO, const void* q, const void* k, const void
   FAB_TRY(check_workspace(workspace, workspace_bytes, B, H, Sq));
   const size_t nk = (size_t)B * H_kv * Sk * D * elem_size(dtype);
   FAB_TRY(check_bwd_device(dO, q, k, v, B, H, H_kv, Sq, Sk, D, dtype));
-  FAB_TRY(check_device_range(workspace, ws_bytes(B, H, Sq), "workspace"));
+  const bool ds = use_ds(workspace_bytes, B, H, H_kv, Sq, Sk, dtype);
+  FAB_TRY(check_device_range(workspace, ds ? ws_bytes_ds(B, H, Sq, Sk) : ws_bytes(B, H, Sq), "workspace"));
   FAB_TRY(check_device_range(dk, nk, "dk"));
   FAB_TRY(check_device_range(dv, nk, "dv"));
-  const fab::BwdParams p =
+  fab::BwdParams p =
       bwd_params(dO, q, k, v, workspace, nullptr, dk, dv, B, H, H_kv, Sq, Sk, causal, window_size, scale);
+  if (ds) set_ds(p, workspace);
   fab::LaunchInfo li;
   FAB_TRY(launched(launch_step2(p, dtype, D, (hipStream_t)stream, true, false, &li), "bwd_dkdv"));
   return FAB_OK;
@@ -439,11 +500,18 @@ fab_status fab_bwd_dq(const void* dO, const void* q, const void* k, const void* 
   FAB_TRY(check_workspace(workspace, workspace_bytes, B, H, Sq));
   const size_t nq = (size_t)B * H * Sq * D * elem_size(dtype);
   FAB_TRY(check_bwd_device(dO, q, k, v, B, H, H_kv, Sq, Sk, D, dtype));
-  FAB_TRY(check_device_range(workspace, ws_bytes(B, H, Sq), "workspace"));
+  const bool ds = use_ds(workspace_bytes, B, H, H_kv, Sq, Sk, dtype);
+  FAB_TRY(check_device_range(workspace, ds ? ws_bytes_ds(B, H, Sq, Sk) : ws_bytes(B, H, Sq), "workspace"));
   FAB_TRY(check_device_range(dq, nq, "dq"));
-  const fab::BwdParams p =
+  fab::BwdParams p =
       bwd_params(dO, q, k, v, workspace, dq, nullptr, nullptr, B, H, H_kv, Sq, Sk, causal, window_size, scale);
   fab::LaunchInfo li;
+  if (ds) {
+    set_ds(p, workspace);
+    FAB_TRY(launched(fab::launch_bwd_dq_ds16(p, dtype, D, (hipStream_t)stream, &li), "bwd_dq"));
+    log_launch(li);
+    return FAB_OK;
+  }
   FAB_TRY(launched(launch_step2(p, dtype, D, (hipStream_t)stream, false, true, &li), "bwd_dq"));
   return FAB_OK;
 }

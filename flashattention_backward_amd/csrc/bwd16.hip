@@ -1,4 +1,7 @@
-// The two step-2 kernels for 16-bit inputs (bf16, fp16), tiled for gfx950.
+// The step-2 kernels for 16-bit inputs (bf16, fp16), tiled for gfx950: the key-tile outer
+// dK/dV kernel, and dQ in one of two ways -- a query-tile outer kernel that recomputes S and dP,
+// or, when the workspace holds room for it, a contraction dQ = scale dS K over the dS values
+// the dK/dV kernel stored ("stored dS").
 //
 // Both kernels stage their streamed operand tiles with direct global->LDS loads
 // (buffer_load_dwordx4 ... lds) into a ring of stage buffers, so the next tiles arrive while
@@ -19,6 +22,17 @@
 #include "launch.h"
 
 namespace fab {
+
+// Cache policy of the stored-dS traffic (gfx950 bits: 1 = sc0, 2 = nt, 16 = sc1): dS is
+// written once and read once, by another kernel, so both sides stream it (nt) rather than
+// let it displace the Q, dO and K tiles that neighbouring workgroups share through the L2
+// (measured: 0.870 against 0.913 ms for the whole backward at B=2, H=32, S=4096, D=128).
+#ifndef FAB_DS_STORE_AUX
+#define FAB_DS_STORE_AUX 2
+#endif
+#ifndef FAB_DS_LOAD_AUX
+#define FAB_DS_LOAD_AUX 2
+#endif
 
 // =======================================================================================
 // dK, dV: key-tile outer (boostr flash_bwd.rs "Step 2": one workgroup per tile of keys).
@@ -105,12 +119,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
 
   f32x16 dk[KB][NDB], dv[KB][NDB];
 #pragma unroll
-  for (int nb = 0; nb < KB; ++nb)
+  for (int nb = 0; nb < KB; ++nb) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       dk[nb][db] = f32x16{};
       dv[nb][db] = f32x16{};
     }
+    mma_ready(dk[nb]);
+    mma_ready(dv[nb]);
+  }
 
   // ---- per-lane LDS offsets
   // A operand (Q or dO rows): row 32 qh + c32, chunk 2 cc + hl
@@ -162,6 +179,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   const rsrc_t rst = make_rsrc(p.stats + (size_t)(b * p.H + g * G) * Sq_pad * 2,
                                (unsigned)((size_t)G * Sq_pad * 8));
 
+  // Stored dS (p.ds set): every dS fragment of the step is also written to the slab of its
+  // query head, for the dQ kernel that follows.  The resource spans the group's G slabs (the
+  // host keeps that below 4 GB).  A lane's 16 bytes of a fragment (key c32, 8 query rows) go
+  // to byte 16 (2 c32 + hl): the two lane halves of one key side by side, which is what the
+  // dQ kernel's transposed LDS reads of 4 keys x 16 rows want.
+  const bool store_ds = p.ds != nullptr;
+  const rsrc_t rds = make_rsrc(store_ds ? (const char*)p.ds + (size_t)(b * p.H + g * G) * p.ds_slab
+                                        : (const char*)p.q,
+                               store_ds ? (unsigned)G * p.ds_slab : 0u);
+  const unsigned ds_voff = 16u * (2 * c32 + hl);
+  const int k32w = nw0 >> 5;
+
   Dma qdma;
   qdma.init(w, lane);
   // Head and tile of the next stage to prefetch, advanced once per issued stage.  Past the
@@ -212,6 +241,23 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   // MFMAs run, so a step starts with them in registers.
   F aq[NC];
   float l2[16], dl[16];
+  // dS of the current step (16-bit, the A operand of dK += dS^T Q), kept until the next step
+  // has stored it when dS is stored; ds_soff is its offset in the group's slabs.
+  F da[KB][2];
+  unsigned ds_soff = 0;
+  bool ds_pending = false;
+  auto store_pending_ds = [&]() {
+    if (store_ds && ds_pending) {
+#pragma unroll
+      for (int nb = 0; nb < KB; ++nb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, da[nb][ks]), rds, ds_voff,
+                                                 ds_soff + (unsigned)(nb * 8192 + ks * 1024),
+                                                 FAB_DS_STORE_AUX);
+    }
+    ds_pending = true;
+  };
   auto load_step_operands = [&](const char* __restrict__ buf) {
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) aq[cc] = lds_frag<T>(buf, a_off[cc]);
@@ -234,10 +280,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   // barrier that ends the step sits before its last MFMAs: by then every read of `cur` has
   // completed, and the next step's operands are read from `nb1` while those MFMAs run.
   auto step_body = [&](const char* __restrict__ cur, const char* __restrict__ vrows,
-                       char* __restrict__ nxt, const char* nb1, int m0) {
+                       char* __restrict__ nxt, const char* nb1, int m0, int hh) {
     unsigned pq_soff, pst_soff;
     next_offsets(pq_soff, pst_soff);
     const int mw0 = m0 + 32 * qh;
+    // The dS fragments of the previous step go out first, before this step's prefetch: the
+    // end-of-step wait counts the loads issued after the next stage's, and with the stores
+    // issued ahead of them it covers stores a whole step old and nothing of the prefetch,
+    // whether or not stores complete in order with loads.
+    store_pending_ds();
+    // dS fragment (nb, ks) of this step: row block mw0 / 16 + ks, key block k32w + nb.
+    ds_soff = (unsigned)hh * p.ds_slab +
+              (unsigned)((((mw0 >> 7) * p.ds_nk32 + k32w) * 8 + ((mw0 >> 4) & 7)) * 1024);
 
     // ---- S = Q K^T for the wave's key blocks; the prefetch is spread over it, one instruction
     // per head-dim slice, so the wave never stalls on a burst of loads.
@@ -291,7 +345,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
     // many as their issue time covers (an exponential with its fma and conversion takes about
     // two thirds of an MFMA's), and never fewer than registers 0..7; the rest run under the
     // dK MFMAs of rows 0..15, which otherwise leave the vector ALU idle.
-    F pa[KB][2], da[KB][2];
+    F pa[KB][2];
     constexpr int NE = 16 * KB;
     constexpr int NE_FIT = NC * KB * 3 / 2;
     constexpr int NE_DP = NE < NE_FIT ? NE : (NE_FIT > 8 * KB ? NE_FIT : 8 * KB);
@@ -410,13 +464,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   for (int s = 0; s < total; ++s) {
     const int nb1 = cb == STAGES - 1 ? 0 : cb + 1;                     // (s + 1) % STAGES
     const int nb2 = STAGES == 2 ? nb1 : (cb >= 1 ? cb - 1 : STAGES - 1);  // (s + STAGES - 1) % STAGES
-    step_body(smem + cb * C::BUF, vrows, smem + nb2 * C::BUF, smem + nb1 * C::BUF, it * BM);
+    step_body(smem + cb * C::BUF, vrows, smem + nb2 * C::BUF, smem + nb1 * C::BUF, it * BM, hh);
     cb = nb1;
     if (++hh == G) {
       hh = 0;
       --it;
     }
   }
+  store_pending_ds();  // the last step's dS
   // the epilogue reuses the staging buffers: every prefetch must have landed
   wait_vm_all();
   barrier_lds();
@@ -598,6 +653,7 @@ __global__ __launch_bounds__(256, (HD <= 128 ? 2 : 1)) void bwd_dq16_kernel(cons
   f32x16 dq[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dq[db] = f32x16{};
+  mma_ready(dq);
 
   int a_off[NC];
 #pragma unroll
@@ -749,6 +805,206 @@ __global__ __launch_bounds__(256, (HD <= 128 ? 2 : 1)) void bwd_dq16_kernel(cons
   }
 }
 
+// =======================================================================================
+// dQ from stored dS: once the dK/dV kernel has written every dS fragment, dQ = scale * dS K is
+// a plain contraction, without recomputing S and dP.  A workgroup owns BM = 128 query rows of
+// one (batch, head), wave w the rows [32 w, 32 w + 32); per step of 64 keys it stages the dS
+// fragments of its rows and the K tile in LDS by direct loads and accumulates dQ in AGPRs.
+// A stored fragment holds, for each of its 32 keys, 16 query rows, two 8-byte runs of four
+// consecutive rows per lane half (see the dK/dV kernel); the MFMA wants one query row per lane
+// and keys along the 8 slots of its operand, so the fragment is read with the transposing LDS
+// read: in a 16-lane group, lane 4 q + c addresses rows 4 c .. 4 c + 3 of key q0 + q, and lane
+// i receives query row i of keys q0 .. q0 + 3.  The dS operand carries keys in natural order
+// (slot t of lane half h: key 8 h + t of the 16-key slice), and so does the K operand, read
+// transposed from the row-major K tile.  dS reaches the kernel cold from HBM while K mostly
+// hits the L2, so the ring is as deep as the LDS allows (one workgroup per CU): loads count
+// in order on one counter, so K and dS must share one prefetch distance.
+// =======================================================================================
+template <int HD, int NKB, int WGS>
+struct DqDs16 {
+  typedef TileLayout<HD> L;
+  static constexpr int BM = 128, BN = 32 * NKB;  // NKB key blocks of 32 per step
+  static constexpr int FRAG = 1024;             // one dS fragment: 32 keys x 16 rows
+  // Row block r of a stage (its NKB fragments) starts at r * RB: the 128 bytes past the
+  // fragments put the two row blocks a wave reads in one instruction on different banks.
+  static constexpr int RB = NKB * FRAG + 128;
+  static constexpr int DSB = 8 * RB;            // dS part of a stage
+  static constexpr int KT = L::bytes(BN);       // K tile
+  static constexpr int BUF = DSB + KT;
+  typedef TileDma<bf16, HD, BN> Dma;            // (the element type only sets the row size)
+  static constexpr int KMAX = Dma::KMAX;
+  static constexpr int SPARE = Dma::kSpare ? 1024 : 0;
+  static constexpr int STAGES_FIT = (160 * 1024 / WGS - SPARE) / BUF;
+  static constexpr int STAGES = STAGES_FIT > 8 ? 8 : STAGES_FIT;
+  static constexpr int LDS = STAGES * BUF + SPARE;
+  static constexpr int NDS = 2 * NKB;           // dS fragments each wave loads per stage
+  static constexpr int ISSUE = KMAX + NDS;      // loads each wave issues per stage
+  static constexpr int OROW = HD * 2 + 16;      // epilogue: row pitch of the 16-bit output tile
+  static_assert(STAGES >= 2, "a double buffer at least");
+  static_assert(4 * 32 * OROW <= LDS, "the output tiles of the four waves fit the staging buffers");
+  static_assert(BUF % 16 == 0 && DSB % 16 == 0 && RB % 256 == 128, "granule alignment, banks");
+};
+
+template <class T, int HD, int NKB, int WGS>
+__global__ __launch_bounds__(256, WGS) void bwd_dq_ds16_kernel(const BwdParams p) {
+  typedef DqDs16<HD, NKB, WGS> C;
+  typedef typename Frag<T>::type F;
+  constexpr int NDB = HD / 32, BM = C::BM, BN = C::BN, STAGES = C::STAGES;
+  typedef typename C::L L;
+
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+  char* const spare = smem + STAGES * C::BUF;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
+  const int lane = tid & 63, c32 = lane & 31, hl = lane >> 5;
+  const int Sq = p.Sq, Sk = p.Sk;
+  const int G = p.H / p.H_kv;
+  const int n_qt = (Sq + BM - 1) / BM;
+
+  const WorkItem wi = map_work(blockIdx.x, p.n_units, p.units_per_xcd);
+  const int b = wi.unit / p.H_kv, g = wi.unit % p.H_kv;
+  const int hq = g * G + wi.step % G;
+  const int tq = wi.step / G;
+  const int it = p.causal ? n_qt - 1 - tq : tq;  // heaviest query tiles first
+  const int m0 = it * BM;
+  const int mw0 = m0 + 32 * w;
+
+  const size_t q_off = (size_t)(b * p.H + hq) * Sq;
+  const T* Kg = (const T*)p.k + (size_t)(b * p.H_kv + g) * Sk * HD;
+
+  f32x16 dq[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dq[db] = f32x16{};
+  mma_ready(dq);
+
+  // Per-lane LDS offsets of the transposed reads.  16-lane group grp = lane / 16: lane half
+  // h = grp / 2 (keys 8 h ..), and sub = grp % 2 selects the wave's second row block (dS) or
+  // the second 16 columns of a 32-column block of K; in the group, lane 4 q + c.
+  const int grp = lane >> 4, hh = grp >> 1, sub = grp & 1, qd = (lane >> 2) & 3, cq = lane & 3;
+  // dS: key 8 hh + 4 sec + qd of a 16-key slice, rows 4 cq .. 4 cq + 3 of row block 2 w + sub;
+  // slice sl adds (sl / 2) fragments and (sl % 2) * 16 keys, sec = 1 four keys.
+  const int ds_off = (2 * w + sub) * C::RB + 32 * (8 * hh + qd) + 16 * (cq & 1) + 8 * (cq >> 1);
+  // K: key row 8 hh + 4 sec + qd of the slice, columns 32 db + 16 sub + 4 cq .. + 3.
+  int k_off[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) {
+      const int r = 8 * hh + 4 * sec + qd;
+      const int col = 32 * db + 16 * sub + 4 * cq;
+      k_off[db][sec] = C::DSB + L::off(r, col >> 3) + 2 * (col & 7);
+    }
+
+  // key tiles holding a key some row of this tile may attend
+  const KeyRange kr{Sk, p.causal, p.win};
+  const int k_lo = kr.lo(m0), k_hi = kr.hi(min(m0 + BM, Sq) - 1);
+  const int j_begin = k_lo / BN;
+  const int j_end = k_hi >= k_lo ? k_hi / BN + 1 : j_begin;
+
+  // The dS fragments of a row block exist (were written by the dK/dV kernel) where the block
+  // sees some key of the key block; the others are never written and read as zeros here.
+  // This lane's row block (2 w + sub of the tile) sees keys [v_lo, v_hi]; rows past Sq carry
+  // nothing (their dQ is not stored), so their block is left empty.
+  const int rb0 = mw0 + 16 * sub;
+  const int v_lo = rb0 < Sq ? kr.lo(rb0) : 1;
+  const int v_hi = rb0 < Sq ? kr.hi(min(rb0 + 15, Sq - 1)) : 0;
+
+  // Loads: the K tile through buffer loads (keys past Sk read as zeros), and wave w's dS
+  // fragments (its two row blocks x the step's key blocks) from the (b, hq) slab.  The
+  // prefetches issued past the last step land in stages nothing reads any more (their
+  // offsets stay inside the slab or read zeros past it).
+  TileDma<T, HD, BN> kdma;
+  kdma.init(w, lane);
+  const rsrc_t rk = make_rsrc(Kg, (unsigned)((size_t)Sk * HD * sizeof(T)));
+  const rsrc_t rds = make_rsrc((const char*)p.ds + (size_t)(b * p.H + hq) * p.ds_slab, p.ds_slab);
+  constexpr unsigned TILEB = BN * HD * sizeof(T);  // source bytes of one key tile
+  const unsigned ds_row = (unsigned)(it * p.ds_nk32) * 8u + 2u * w;  // in fragments
+  auto issue_part = [&](int j, char* buf, int k) {
+    if (k < C::KMAX) kdma.issue(k, buf + C::DSB, rk, (unsigned)j * TILEB, spare, lane);
+    if (k < C::NDS) {
+      const int rbw = k % 2, kb = k / 2;
+      b2lds16<FAB_DS_LOAD_AUX>(rds, 16u * lane, (ds_row + (unsigned)(NKB * j + kb) * 8u + rbw) * 1024u,
+                               buf + (2 * w + rbw) * C::RB + kb * C::FRAG);
+    }
+  };
+  constexpr int NPART = C::KMAX > C::NDS ? C::KMAX : C::NDS;
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+#pragma unroll
+    for (int k = 0; k < NPART; ++k) issue_part(j_begin + st, smem + st * C::BUF, k);
+  wait_vm_le<C::ISSUE * (STAGES - 2)>();  // stage 0 has landed
+  barrier_lds();
+
+  // One step of BN keys on stage `cur`; `nxt` receives the stage STAGES - 1 steps ahead.
+  auto step_body = [&](const char* __restrict__ cur, char* __restrict__ nxt, int j) {
+    const int n0 = j * BN;
+    // Steps where some row of the wave may not see some key read the validity of each dS
+    // fragment; elsewhere every fragment was written.
+    const bool edge = kr.hi(mw0) < n0 + BN - 1 || kr.lo(mw0 + 31) > n0;
+    bool valid[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int key0 = n0 + 32 * kb;
+      valid[kb] = v_lo <= v_hi && key0 <= v_hi && key0 + 31 >= v_lo;
+    }
+    int part = 0;
+#pragma unroll
+    for (int sl = 0; sl < 2 * NKB; ++sl) {
+      const int kb = sl >> 1, ks = sl & 1;
+      const int so = kb * C::FRAG + ks * 512;  // slice offset in a row block
+      F a = lds_frag_tr<T>(cur, ds_off + so, ds_off + so + 128);
+      if (edge && !valid[kb]) a = zero8<T>();
+      const int ro = L::rows(16 * sl);
+      F bk = lds_frag_tr<T>(cur, k_off[0][0] + ro, k_off[0][1] + ro);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        F bk_n;
+        if (db + 1 < NDB) bk_n = lds_frag_tr<T>(cur, k_off[db + 1][0] + ro, k_off[db + 1][1] + ro);
+        if (db == 0) mma_a<true>(dq[db], a, bk);  // first use of this slice's dS operand
+        else mma_a<false>(dq[db], a, bk);
+        if (part < NPART) issue_part(j + STAGES - 1, nxt, part++);
+        if (db + 1 < NDB) bk = bk_n;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    while (part < NPART) issue_part(j + STAGES - 1, nxt, part++);
+  };
+
+  int cb = 0;  // buffer of step j
+  for (int j = j_begin; j < j_end; ++j) {
+    const int pb = cb == 0 ? STAGES - 1 : cb - 1;  // (j + STAGES - 1) % STAGES
+    step_body(smem + cb * C::BUF, smem + pb * C::BUF, j);
+    wait_vm_le<C::ISSUE * (STAGES - 2)>();  // stage j + 1 has landed
+    barrier_lds();
+    cb = cb == STAGES - 1 ? 0 : cb + 1;
+  }
+  wait_vm_all();  // no prefetch of this wave is still writing LDS ...
+  barrier_lds();  // ... nor of any other: the stage buffers are free for the output tiles
+
+  // ---- epilogue: dQ = scale * acc, staged through a row-major tile per wave and stored by
+  // whole rows (16 bytes per lane), as in the recomputing dQ kernel.
+  mma_drain(dq);
+  char* const otile = smem + w * (32 * C::OROW);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * hl + (r & 3);
+      *reinterpret_cast<T*>(otile + row * C::OROW + 2 * (32 * db + c32)) = (T)(dq[db][r] * p.scale);
+    }
+  asm volatile("" ::: "memory");  // the wave reads back only what it wrote, in order
+  T* dQg = (T*)p.dq + q_off * HD;
+  constexpr int CPR = HD / 8;  // 16-byte chunks per row
+#pragma unroll
+  for (int i = 0; i < CPR / 2; ++i) {
+    const int q = 64 * i + lane, row = q / CPR, ch = q % CPR;
+    typedef T v8 __attribute__((ext_vector_type(8)));
+    const v8 val = *reinterpret_cast<const v8*>(otile + row * C::OROW + 16 * ch);
+    if (mw0 + row < Sq) *reinterpret_cast<v8*>(dQg + (size_t)(mw0 + row) * HD + 8 * ch) = val;
+  }
+}
+
 template <class T, int HD, bool WIDE>
 static hipError_t go_dkdv_cfg(const BwdParams& p, hipStream_t s, LaunchInfo* info) {
   typedef Dkdv16<HD, WIDE> C;
@@ -803,6 +1059,39 @@ static hipError_t go_dq(const BwdParams& p, hipStream_t s, LaunchInfo* info) {
   return hipGetLastError();
 }
 
+// Key blocks per step of the stored-dS dQ kernel and its workgroups per CU (the stage ring
+// fills the LDS share of one workgroup).  Measured at B=2, H=32, S=4096, D=128: 64-key steps
+// with two workgroups per CU (two stages each) 0.246 ms; one workgroup with four stages 0.267;
+// 32-key steps 0.255 (two workgroups, four stages) and 0.280 (one, eight stages).
+#ifndef FAB_DQDS_NKB
+#define FAB_DQDS_NKB 2
+#endif
+#ifndef FAB_DQDS_WGS
+#define FAB_DQDS_WGS 2
+#endif
+
+template <class T, int HD>
+static hipError_t go_dq_ds(const BwdParams& p, hipStream_t s, LaunchInfo* info) {
+  constexpr int NKB = FAB_DQDS_NKB, WGS = HD == 256 ? 1 : FAB_DQDS_WGS;
+  typedef DqDs16<HD, NKB, WGS> C;
+  const int n_qt = (p.Sq + C::BM - 1) / C::BM;
+  const int grid = p.n_units * (p.H / p.H_kv) * n_qt;
+  if (info) *info = LaunchInfo{"bwd_dq_ds16", grid, 256, C::LDS};
+  hipLaunchKernelGGL((bwd_dq_ds16_kernel<T, HD, NKB, WGS>), dim3(grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <class T>
+static hipError_t dq_ds_hd(const BwdParams& p, int hd, hipStream_t s, LaunchInfo* info) {
+  switch (hd) {
+    case 32: return go_dq_ds<T, 32>(p, s, info);
+    case 64: return go_dq_ds<T, 64>(p, s, info);
+    case 96: return go_dq_ds<T, 96>(p, s, info);
+    case 128: return go_dq_ds<T, 128>(p, s, info);
+    default: return go_dq_ds<T, 256>(p, s, info);
+  }
+}
+
 template <class T>
 static hipError_t dkdv_hd(const BwdParams& p, int hd, hipStream_t s, LaunchInfo* info) {
   switch (hd) {
@@ -831,6 +1120,10 @@ hipError_t launch_bwd_dkdv16(const BwdParams& p, int dt, int hd, hipStream_t s, 
 
 hipError_t launch_bwd_dq16(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info) {
   return dt == kBF16 ? dq_hd<bf16>(p, hd, s, info) : dq_hd<f16>(p, hd, s, info);
+}
+
+hipError_t launch_bwd_dq_ds16(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info) {
+  return dt == kBF16 ? dq_ds_hd<bf16>(p, hd, s, info) : dq_ds_hd<f16>(p, hd, s, info);
 }
 
 }  // namespace fab

@@ -25,6 +25,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -87,6 +88,22 @@ __device__ __forceinline__ void mma_drain(f32x16 (&a)[3]) {
 __device__ __forceinline__ void mma_drain(f32x16 (&a)[1]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(a[0]));
 }
+// Two wait states after the accumulators were last written by vector instructions (their
+// zero initialisation, which the compiler may emit as AGPR moves anywhere before the first
+// MFMA): the asm reads and writes them, so every such write precedes it, and no inline-asm
+// MFMA, which the compiler's hazard handling does not see, can follow a write too closely.
+__device__ __forceinline__ void mma_ready(f32x16 (&a)[8]) {
+  asm volatile("s_nop 1" : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]), "+a"(a[4]), "+a"(a[5]),
+               "+a"(a[6]), "+a"(a[7]));
+}
+__device__ __forceinline__ void mma_ready(f32x16 (&a)[4]) {
+  asm volatile("s_nop 1" : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]));
+}
+__device__ __forceinline__ void mma_ready(f32x16 (&a)[3]) {
+  asm volatile("s_nop 1" : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]));
+}
+__device__ __forceinline__ void mma_ready(f32x16 (&a)[2]) { asm volatile("s_nop 1" : "+a"(a[0]), "+a"(a[1])); }
+__device__ __forceinline__ void mma_ready(f32x16 (&a)[1]) { asm volatile("s_nop 1" : "+a"(a[0])); }
 // The same with the accumulator in VGPRs, as volatile asm: the statements keep their order
 // relative to each other and to order_point(), which lets a loop state exactly where vector
 // work goes between MFMAs.  mma_v0 starts a contraction (accumulator input 0); its output
@@ -323,9 +340,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, unsigned bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// AUX: the cache-policy bits of the load (gfx950: 1 = sc0, 2 = nt, 16 = sc1).
+template <int AUX = 0>
 __device__ __forceinline__ void b2lds16(rsrc_t r, unsigned voff, unsigned soff, char* lds_wave_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_char*)lds_wave_base,
-                                           16, voff, soff, 0, 0);
+                                           16, voff, soff, 0, AUX);
 }
 
 // Copy rows [row0, row0 + ROWS) of a row-major [*, HD] tensor slice (rows 0 .. last_row,

@@ -15,6 +15,11 @@ constexpr float kLog2eHost = 1.4426950408889634f;
 constexpr int kStatsRows = 64;
 inline int stats_rows(int Sq) { return (Sq + kStatsRows - 1) / kStatsRows * kStatsRows; }
 
+// Rows and keys a dS slab covers: every row block and key block either step-2 kernel may
+// touch (query tiles of up to 128 rows, key tiles of up to 256 keys).
+inline long long ds_rows(int Sq) { return (Sq + 127LL) / 128 * 128; }
+inline long long ds_keys(int Sk) { return (Sk + 255LL) / 256 * 256; }
+
 struct PreParams {
   const void* dO;
   const void* o;
@@ -53,6 +58,14 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
+  // Stored dS (16-bit path; null when dQ recomputes dS): the dK/dV kernel writes every dS
+  // fragment it forms, the dQ kernel that follows reads them back.  Per (b, h) a slab of
+  // ds_slab bytes: 1 KB fragments of 32 keys x 16 query rows (see bwd16.hip), the fragment of
+  // row block r (rows 16 r ..) and key block k (keys 32 k ..) at byte
+  // ((r / 8 * ds_nk32 + k) * 8 + r % 8) * 1024 of the slab.
+  void* ds;
+  unsigned ds_slab;  // bytes per (b, h): ds_rows(Sq) * ds_keys(Sk) * 2
+  int ds_nk32;       // key blocks per slab row: ds_keys(Sk) / 32
   int B, H, H_kv, Sq, Sk, Sq_pad;
   int causal;
   int win;            // sliding window in keys, 0 = none (see KeyRange in common.h)
@@ -76,5 +89,7 @@ hipError_t launch_bwd_dkdv(const BwdParams& p, int dt, int hd, hipStream_t s, La
 hipError_t launch_bwd_dq(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info);
 hipError_t launch_bwd_dkdv16(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info);
 hipError_t launch_bwd_dq16(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info);
+// dQ = scale * dS K from the dS fragments the dK/dV kernel stored (p.ds set).
+hipError_t launch_bwd_dq_ds16(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info);
 
 }  // namespace fab

@@ -74,15 +74,31 @@ const char* fab_version(void);
 const char* fab_last_error(void);
 
 /*
- * Bytes of device workspace the backward needs for these sizes (0 if the sizes are invalid).
- * Layout, as written by the preprocessing step: float32 pairs
+ * Bytes of device workspace for the fastest mode of the backward at these sizes (0 if the
+ * sizes are invalid); fab_bwd_workspace_bytes_min gives the least fab_bwd accepts.
+ *
+ * The workspace selects how dQ is formed.  With at least fab_bwd_workspace_bytes bytes, for
+ * float16 / bfloat16 inputs whose dS buffer fits (below), the dK/dV kernel also stores every
+ * dS value it forms and dQ = scale * dS K reads them back ("stored dS": 10 D FLOPs per allowed
+ * pair instead of 14 D, for 2 bytes of HBM written and read per pair).  With less (at least
+ * fab_bwd_workspace_bytes_min), or for float32, dQ recomputes S and dP ("recompute").  Both
+ * give the same result up to float rounding order; each is deterministic.
+ *
+ * Layout.  From byte 0, as written by the preprocessing step, float32 pairs
  *   ws[((b * H + h) * Sq_pad + i) * 2 + 0] = lse[b, h, i] * log2(e)
  *   ws[((b * H + h) * Sq_pad + i) * 2 + 1] = D[b, h, i] = sum_d dO[b,h,i,d] * o[b,h,i,d]
  * with Sq_pad = Sq rounded up to a multiple of 64; rows i >= Sq, and rows whose lse is -inf
- * (rows with no allowed key), hold +inf in place of lse * log2(e).  fab_bwd
- * overwrites the workspace on every call; its contents on entry do not matter.
+ * (rows with no allowed key), hold +inf in place of lse * log2(e).  The statistics take
+ * fab_bwd_workspace_bytes_min bytes (B * H * Sq_pad * 8, rounded up to 256).  Stored dS
+ * follows from the next 4096-byte boundary: per (b, h), Sq rounded up to 128 times Sk rounded
+ * up to 256 dtype values, in fragments of 32 keys x 16 query rows in the kernels' own order.
+ * Stored dS is taken when that slab is at most 2 GiB, the H / H_kv slabs of a kv-head group
+ * stay below 4 GiB and all slabs together at most 32 GiB (for example 2.1 GB at B=2, H=32,
+ * S=4096).  fab_bwd overwrites the workspace on every call; its contents on entry do not
+ * matter.
  */
 size_t fab_bwd_workspace_bytes(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype);
+size_t fab_bwd_workspace_bytes_min(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype);
 
 /*
  * Supporting forward (boostr autograd_attention.rs, var_flash_attention: the forward
@@ -119,9 +135,13 @@ fab_status fab_bwd_preprocess(const void* dO, const void* o, const float* lse,
  * Inputs dO, q, o: [B, num_heads, Sq, D]; k, v: [B, num_kv_heads, Sk, D]; lse as produced
  * by fab_fwd.  Outputs dq [B, num_heads, Sq, D], dk and dv [B, num_kv_heads, Sk, D], all in
  * `dtype`; they need no initialisation and every element is written (rows the mask never
- * reaches get 0).  workspace: at least fab_bwd_workspace_bytes(...) bytes of device
- * memory.  All pointers 16-byte aligned; outputs must not overlap inputs or each other.
- * Deterministic: no atomics, identical inputs give bitwise identical outputs.
+ * reaches get 0).  workspace: at least fab_bwd_workspace_bytes_min(...) bytes of device
+ * memory; with at least fab_bwd_workspace_bytes(...) the stored-dS mode runs where it applies
+ * (see there).  All pointers 16-byte aligned; outputs must not overlap inputs or each other.
+ * Deterministic: no atomics, identical inputs and workspace size give bitwise identical
+ * outputs.  Launches: stored dS -- step 1, the dK/dV kernel (which also writes dS), then
+ * dQ = scale * dS K; recompute (16-bit) -- the dQ kernel (with step 1 folded into its
+ * prologue), then the dK/dV kernel; float32 -- step 1, dK/dV, dQ.
  */
 fab_status fab_bwd(const void* dO, const void* q, const void* k, const void* v,
                    const void* o, const float* lse, void* dq, void* dk, void* dv,
@@ -150,13 +170,17 @@ fab_status fab_bwd_noalloc(const void* dO, const void* q, const void* k, const v
 /*
  * The two kernels of step 2 on their own, for inspection and per-kernel timing; fab_bwd
  * runs them itself after step 1.  `workspace` must hold what fab_bwd_preprocess wrote for
- * the same dO, o and lse.  Other arguments as for fab_bwd.
+ * the same dO, o and lse.  The workspace size selects the mode as for fab_bwd.  Other
+ * arguments as for fab_bwd.
  *   fab_bwd_dkdv writes dk, dv (key-tile outer; each workgroup owns a tile of keys and
- *                sums over every query head of its kv-head group).
- *   fab_bwd_dq   writes dq (query-tile outer; recomputes S and dP for its query rows).
+ *                sums over every query head of its kv-head group), and in the stored-dS mode
+ *                also dS into the workspace.
+ *   fab_bwd_dq   writes dq (query-tile outer): in the stored-dS mode from the dS that
+ *                fab_bwd_dkdv stored in the same workspace for the same inputs; otherwise it
+ *                recomputes S and dP for its query rows.
  */
 fab_status fab_bwd_dkdv(const void* dO, const void* q, const void* k, const void* v,
-                        const void* workspace, size_t workspace_bytes, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, void* dk, void* dv,
                         int B, int num_heads, int num_kv_heads, int Sq, int Sk, int D,
                         int dtype, int causal, int window_size, float scale, void* stream);
 fab_status fab_bwd_dq(const void* dO, const void* q, const void* k, const void* v,

@@ -65,24 +65,28 @@ def window_span_ranges(c: int, e: int, S: int, W: int):
     return (lo, e), (lo, e - W + 1 if e < S else S)
 
 
-def run_gpu(fab, q, k, v, do, causal, scale, window=0):
-    """End-to-end HIP path: fwd then bwd, all inputs resident on cuda:0."""
+def run_gpu(fab, q, k, v, do, causal, scale, window=0, store_ds=True):
+    """End-to-end HIP path: fwd then bwd, all inputs resident on cuda:0.  store_ds selects the
+    backward's mode through its workspace size (stored dS where it applies, else recompute)."""
     import torch
     dev = torch.device("cuda:0")
     qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
     o, lse = fab.fwd(qd, kd, vd, causal=causal, scale=scale, window_size=window)
-    dq, dk, dv = fab.bwd(dod, qd, kd, vd, o, lse, causal=causal, scale=scale, window_size=window)
+    dq, dk, dv = fab.bwd(dod, qd, kd, vd, o, lse, causal=causal, scale=scale, window_size=window,
+                         store_ds=store_ds)
     torch.cuda.synchronize()
     return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
 
 
-def check_end_to_end(fab, w: workloads.Workload, groups=None, jobs: int = 1, check_fwd=True):
+def check_end_to_end(fab, w: workloads.Workload, groups=None, jobs: int = 1, check_fwd=True,
+                     store_ds=True):
     """GPU fwd+bwd against oracle fwd+bwd on the same rounded inputs.  With ``groups`` only
     those (b, kv head) groups are compared (full-size runs)."""
     say(f"[case] {w.name} dtype={w.dtype} B={w.B} H={w.H} H_kv={w.H_kv} Sq={w.Sq} Sk={w.Sk} "
-        f"D={w.D} causal={w.causal} window={w.window} seed={w.seed} groups={groups}")
+        f"D={w.D} causal={w.causal} window={w.window} seed={w.seed} groups={groups} "
+        f"mode={'stored-dS' if store_ds else 'recompute'}")
     q, k, v, do = workloads.make_inputs(w)
-    out = run_gpu(fab, q, k, v, do, w.causal, w.scale, w.window)
+    out = run_gpu(fab, q, k, v, do, w.causal, w.scale, w.window, store_ds=store_ds)
     if groups is None:
         ref = oracle.attention_grads(q, k, v, do, w.causal, w.scale, window=w.window)
         pairs = [("dq", out["dq"], ref["dq"]), ("dk", out["dk"], ref["dk"]), ("dv", out["dv"], ref["dv"])]

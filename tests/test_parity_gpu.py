@@ -25,10 +25,15 @@ REDUCED = {
 }
 
 
+MODES = [True, False]  # store_ds: the stored-dS mode, then the recompute mode
+MODE_IDS = ["stored_ds", "recompute"]
+
+
+@pytest.mark.parametrize("store_ds", MODES, ids=MODE_IDS)
 @pytest.mark.parametrize("name", list(REDUCED))
-def test_named_workloads_reduced(fab, name):
+def test_named_workloads_reduced(fab, name, store_ds):
     w = workloads.scaled(workloads.get(name), **REDUCED[name])
-    check_end_to_end(fab, w)
+    check_end_to_end(fab, w, store_ds=store_ds)
 
 
 SHAPES = [
@@ -46,11 +51,12 @@ SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("store_ds", MODES, ids=MODE_IDS)
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
-def test_shapes_and_edges(fab, shape):
+def test_shapes_and_edges(fab, shape, store_ds):
     dt, B, H, H_kv, Sq, Sk, D, causal = shape
     w = workloads.Workload(f"edge_{dt}", dt, B, H, H_kv, Sq, Sk, D, causal, seed=1000 + Sq + 7 * Sk)
-    check_end_to_end(fab, w)
+    check_end_to_end(fab, w, store_ds=store_ds)
 
 
 @pytest.mark.parametrize("scale", [-0.2, 0.0, 1e-3, 0.5])
@@ -90,15 +96,65 @@ def test_isolated_backward(fab, dt):
         assert_close(name, to_np64(g), r, dt)
 
 
-def test_deterministic(fab):
+@pytest.mark.parametrize("store_ds", MODES, ids=MODE_IDS)
+def test_deterministic(fab, store_ds):
     import torch
     w = workloads.Workload("det", "bf16", 1, 8, 2, 300, 300, 128, True, seed=5)
-    say("[case] determinism")
+    say(f"[case] determinism store_ds={store_ds}")
     q, k, v, do = workloads.make_inputs(w)
-    a = run_gpu(fab, q, k, v, do, True, w.scale)
-    b = run_gpu(fab, q, k, v, do, True, w.scale)
+    a = run_gpu(fab, q, k, v, do, True, w.scale, store_ds=store_ds)
+    b = run_gpu(fab, q, k, v, do, True, w.scale, store_ds=store_ds)
     for key in ("o", "lse", "dq", "dk", "dv"):
         assert torch.equal(a[key], b[key]), key
+
+
+def test_modes_agree(fab):
+    """The two modes run the same dK/dV kernel.  dV depends only on P and is bitwise equal;
+    dK also depends on D, which the two modes sum in different orders (the preprocess kernel,
+    or the recomputing dQ kernel's prologue), and dQ is formed differently: both agree with
+    the other mode to the tolerances."""
+    import torch
+    w = workloads.Workload("modes", "bf16", 2, 8, 2, 333, 333, 128, True, seed=15)
+    say("[case] stored dS vs recompute")
+    q, k, v, do = workloads.make_inputs(w)
+    a = run_gpu(fab, q, k, v, do, True, w.scale, store_ds=True)
+    b = run_gpu(fab, q, k, v, do, True, w.scale, store_ds=False)
+    assert torch.equal(a["dv"], b["dv"])
+    assert_close("dk", to_np64(a["dk"]), to_np64(b["dk"]), "bf16")
+    assert_close("dq", to_np64(a["dq"]), to_np64(b["dq"]), "bf16")
+
+
+@pytest.mark.parametrize("dt,D,causal,win", [("bf16", 128, True, 0), ("fp16", 64, False, 0),
+                                             ("bf16", 96, True, 70), ("fp16", 256, True, 0)])
+def test_step_entry_points_stored_ds(fab, dt, D, causal, win):
+    """fab_bwd_preprocess, fab_bwd_dkdv and fab_bwd_dq called one by one with the stored-dS
+    workspace (the route bench.py times kernel by kernel): dkdv stores dS, dq reads it."""
+    import ctypes
+    import torch
+    w = workloads.Workload(f"steps_{dt}", dt, 1, 4, 2, 211, 245, D, causal, seed=61, window=win)
+    say(f"[case] step entry points, stored dS: {dt} D={D} causal={causal} window={win}")
+    q, k, v, do = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
+    o, lse = fab.fwd(qd, kd, vd, causal=causal, scale=w.scale, window_size=win)
+    L = fab.lib()
+    code = fab.DTYPE_CODES[str(qd.dtype).replace("torch.", "")]
+    nb = fab.bwd_workspace_bytes(w.B, w.H, w.H_kv, w.Sq, w.Sk, D, code)
+    assert nb > fab.bwd_workspace_bytes(w.B, w.H, w.H_kv, w.Sq, w.Sk, D, code, store_ds=False)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    dims = (w.B, w.H, w.H_kv, w.Sq, w.Sk, D, code, int(causal), win, float(w.scale))
+    assert L.fab_bwd_preprocess(dod.data_ptr(), o.data_ptr(), lse.data_ptr(), ws.data_ptr(), nb,
+                                w.B, w.H, w.Sq, D, code, st) == 0
+    assert L.fab_bwd_dkdv(dod.data_ptr(), qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), ws.data_ptr(),
+                          nb, dk.data_ptr(), dv.data_ptr(), *dims, st) == 0
+    assert L.fab_bwd_dq(dod.data_ptr(), qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), ws.data_ptr(),
+                        nb, dq.data_ptr(), *dims, st) == 0
+    torch.cuda.synchronize()
+    ref = oracle.attention_grads(q, k, v, do, causal, w.scale, window=win)
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert_close(name, to_np64(g), ref[name], dt)
 
 
 def test_causal_zero_rows_and_invariants(fab):

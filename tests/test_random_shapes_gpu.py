@@ -34,8 +34,9 @@ def draw_cases(n=24, seed=20261202):
 CASES = draw_cases()
 
 
+@pytest.mark.parametrize("store_ds", [True, False], ids=["stored_ds", "recompute"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
-def test_random_shape_parity(fab, case):
+def test_random_shape_parity(fab, case, store_ds):
     dt, B, H, H_kv, Sq, Sk, D, causal, W, seed = case
     w = workloads.Workload(f"rand_{dt}", dt, B, H, H_kv, Sq, Sk, D, causal, seed=seed, window=W)
-    check_end_to_end(fab, w)
+    check_end_to_end(fab, w, store_ds=store_ds)
