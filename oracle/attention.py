@@ -187,11 +187,13 @@ def _serial(args):
 
 
 def grads_for_groups(q, k, v, do, causal: bool, scale: float, groups, jobs: int = 1,
-                     window: int = 0):
+                     window: int = 0, start_method: str = "fork"):
     """attention_grads over several (b, g) groups, optionally in a process pool.
 
     With jobs > 1 each worker process receives only its group's slices and uses one BLAS
-    thread; with jobs <= 1 the groups run one after another in this process.  Returns
+    thread ("spawn" starts clean interpreters, for callers whose process holds state a
+    forked child should not inherit); with jobs <= 1 the groups run one after another in
+    this process.  Returns
     {(b, g): result dict with the group's slices: o, lse, delta [G,Sq(,D)], dq [G,Sq,D],
     dk, dv [Sk,D]}.
     """
@@ -207,7 +209,7 @@ def grads_for_groups(q, k, v, do, causal: bool, scale: float, groups, jobs: int 
         outs = [_serial(t)[1] for t in tasks]  # one process, BLAS threads as configured
     else:
         import multiprocessing as mp
-        ctx = mp.get_context("fork")
+        ctx = mp.get_context(start_method)
         pool = ctx.Pool(jobs)
         try:
             outs = [r[1] for r in pool.map(_worker, tasks)]
