@@ -807,50 +807,69 @@ __global__ __launch_bounds__(256, (HD <= 128 ? 2 : 1)) void bwd_dq16_kernel(cons
 
 // =======================================================================================
 // dQ from stored dS: once the dK/dV kernel has written every dS fragment, dQ = scale * dS K is
-// a plain contraction, without recomputing S and dP.  A workgroup owns BM = 128 query rows of
-// one (batch, head), wave w the rows [32 w, 32 w + 32); per step of 64 keys it stages the dS
-// fragments of its rows and the K tile in LDS by direct loads and accumulates dQ in AGPRs.
-// A stored fragment holds, for each of its 32 keys, 16 query rows, two 8-byte runs of four
-// consecutive rows per lane half (see the dK/dV kernel); the MFMA wants one query row per lane
+// a plain contraction, without recomputing S and dP.  A workgroup of eight waves owns 256
+// query-row slots -- 128 rows of two query heads of one kv-head group when the group has an
+// even number of heads, else 256 rows of one head -- and each wave 32 rows of one head.  Per
+// step of 64 keys it stages the K tile, which all eight waves share, and each wave its own dS
+// fragments in LDS by direct loads, and accumulates dQ in AGPRs.  The kernel streams dS from
+// HBM once; what it moves besides is the K tile of every step, so a workgroup covers as many
+// rows per K tile as the LDS allows.
+// A stored fragment holds, for each of its 32 keys, 16 query rows: two 8-byte runs of four
+// consecutive rows per lane half (see the dK/dV kernel).  The MFMA wants one query row per lane
 // and keys along the 8 slots of its operand, so the fragment is read with the transposing LDS
 // read: in a 16-lane group, lane 4 q + c addresses rows 4 c .. 4 c + 3 of key q0 + q, and lane
 // i receives query row i of keys q0 .. q0 + 3.  The dS operand carries keys in natural order
-// (slot t of lane half h: key 8 h + t of the 16-key slice), and so does the K operand, read
-// transposed from the row-major K tile.  dS reaches the kernel cold from HBM while K mostly
-// hits the L2, so the ring is as deep as the LDS allows (one workgroup per CU): loads count
-// in order on one counter, so K and dS must share one prefetch distance.
+// (slot t of lane half h: key 8 h + t of a 16-key slice), and so does the K operand, read
+// transposed from the row-major K tile.
 // =======================================================================================
-template <int HD, int NKB, int WGS>
+
+// K tile of a stored-dS step: 64 rows of HD elements without padding, 16-byte chunk c of row r
+// at r * 2 HD + 16 * (c ^ kswz(r)).  A transposed half-wave read (4 consecutive rows, 64 bytes
+// of each) then covers four different 16-bank windows: rows of 256 or 512 bytes start on the
+// same bank and are spread by the XOR, rows of 128 bytes alternate halves of the bank cycle
+// and the XOR spreads row pairs, and rows of 64 or 192 bytes fall on distinct windows as they
+// are.  kswz(r) depends only on r mod 4, so a slice of 16 rows further is a constant offset.
+template <int HD>
+__device__ __forceinline__ int kswz(int r) {
+  if constexpr (HD == 128 || HD == 256) return 4 * (r & 3);
+  else if constexpr (HD == 64) return 4 * ((r >> 1) & 1);
+  else return 0;
+}
+
+template <int HD>
 struct DqDs16 {
-  typedef TileLayout<HD> L;
-  static constexpr int BM = 128, BN = 32 * NKB;  // NKB key blocks of 32 per step
+  static constexpr int NW = 8;                  // waves
+  static constexpr int ROWS = 32 * NW;          // query-row slots of a workgroup
+  static constexpr int BN = 64;                 // keys per step
   static constexpr int FRAG = 1024;             // one dS fragment: 32 keys x 16 rows
-  // Row block r of a stage (its NKB fragments) starts at r * RB: the 128 bytes past the
+  // Row block r of a stage (its two fragments) starts at r * RB: the 128 bytes past the
   // fragments put the two row blocks a wave reads in one instruction on different banks.
-  static constexpr int RB = NKB * FRAG + 128;
-  static constexpr int DSB = 8 * RB;            // dS part of a stage
-  static constexpr int KT = L::bytes(BN);       // K tile
+  static constexpr int RB = 2 * FRAG + 128;
+  static constexpr int DSB = 2 * NW * RB;       // dS part of a stage
+  static constexpr int ROWB = 2 * HD;           // bytes per K row (16-bit elements)
+  static constexpr int CPR = HD / 8;            // 16-byte chunks per K row
+  static constexpr int KT = BN * ROWB;          // K tile
+  static constexpr int KNI = KT / 1024;         // 1 KB direct loads per K tile
+  static constexpr int KMAX = (KNI + NW - 1) / NW;  // ... issued by each wave
+  static constexpr bool kSpare = NW * KMAX > KNI;   // waves past the tile load into `spare`
+  static constexpr int SPARE = kSpare ? 1024 : 0;
   static constexpr int BUF = DSB + KT;
-  typedef TileDma<bf16, HD, BN> Dma;            // (the element type only sets the row size)
-  static constexpr int KMAX = Dma::KMAX;
-  static constexpr int SPARE = Dma::kSpare ? 1024 : 0;
-  static constexpr int STAGES_FIT = (160 * 1024 / WGS - SPARE) / BUF;
-  static constexpr int STAGES = STAGES_FIT > 8 ? 8 : STAGES_FIT;
+  static constexpr int STAGES_FIT = (160 * 1024 - SPARE) / BUF;
+  static constexpr int STAGES = STAGES_FIT > 4 ? 4 : STAGES_FIT;
   static constexpr int LDS = STAGES * BUF + SPARE;
-  static constexpr int NDS = 2 * NKB;           // dS fragments each wave loads per stage
-  static constexpr int ISSUE = KMAX + NDS;      // loads each wave issues per stage
+  static constexpr int ISSUE = KMAX + 4;        // loads each wave issues per stage
   static constexpr int OROW = HD * 2 + 16;      // epilogue: row pitch of the 16-bit output tile
+  static_assert(KT % 1024 == 0, "whole direct loads per K tile");
   static_assert(STAGES >= 2, "a double buffer at least");
-  static_assert(4 * 32 * OROW <= LDS, "the output tiles of the four waves fit the staging buffers");
-  static_assert(BUF % 16 == 0 && DSB % 16 == 0 && RB % 256 == 128, "granule alignment, banks");
+  static_assert(NW * 32 * OROW <= LDS, "the output tiles of the waves fit the staging buffers");
+  static_assert(BUF % 16 == 0 && RB % 256 == 128, "granule alignment, banks");
 };
 
-template <class T, int HD, int NKB, int WGS>
-__global__ __launch_bounds__(256, WGS) void bwd_dq_ds16_kernel(const BwdParams p) {
-  typedef DqDs16<HD, NKB, WGS> C;
+template <class T, int HD>
+__global__ __launch_bounds__(512, 1) void bwd_dq_ds16_kernel(const BwdParams p) {
+  typedef DqDs16<HD> C;
   typedef typename Frag<T>::type F;
-  constexpr int NDB = HD / 32, BM = C::BM, BN = C::BN, STAGES = C::STAGES;
-  typedef typename C::L L;
+  constexpr int NDB = HD / 32, BN = C::BN, STAGES = C::STAGES, NW = C::NW;
 
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
   char* const spare = smem + STAGES * C::BUF;
@@ -860,15 +879,19 @@ __global__ __launch_bounds__(256, WGS) void bwd_dq_ds16_kernel(const BwdParams p
   const int lane = tid & 63, c32 = lane & 31, hl = lane >> 5;
   const int Sq = p.Sq, Sk = p.Sk;
   const int G = p.H / p.H_kv;
-  const int n_qt = (Sq + BM - 1) / BM;
+  // Two heads of the group per workgroup when G is even (128 rows each), else one (256 rows).
+  const int NH = (G & 1) ? 1 : 2;
+  const int RPH = C::ROWS / NH;                 // rows per head in the workgroup
+  const int WPH = NW / NH;                      // waves per head
+  const int n_qt = (Sq + RPH - 1) / RPH;
 
   const WorkItem wi = map_work(blockIdx.x, p.n_units, p.units_per_xcd);
   const int b = wi.unit / p.H_kv, g = wi.unit % p.H_kv;
-  const int hq = g * G + wi.step % G;
-  const int tq = wi.step / G;
+  const int hs = wi.step % (G / NH), tq = wi.step / (G / NH);
   const int it = p.causal ? n_qt - 1 - tq : tq;  // heaviest query tiles first
-  const int m0 = it * BM;
-  const int mw0 = m0 + 32 * w;
+  const int hq = g * G + hs * NH + w / WPH;      // this wave's query head
+  const int m0 = it * RPH;
+  const int mw0 = m0 + 32 * (w % WPH);           // this wave's first row
 
   const size_t q_off = (size_t)(b * p.H + hq) * Sq;
   const T* Kg = (const T*)p.k + (size_t)(b * p.H_kv + g) * Sk * HD;
@@ -893,42 +916,50 @@ __global__ __launch_bounds__(256, WGS) void bwd_dq_ds16_kernel(const BwdParams p
     for (int sec = 0; sec < 2; ++sec) {
       const int r = 8 * hh + 4 * sec + qd;
       const int col = 32 * db + 16 * sub + 4 * cq;
-      k_off[db][sec] = C::DSB + L::off(r, col >> 3) + 2 * (col & 7);
+      k_off[db][sec] = C::DSB + r * C::ROWB + 16 * ((col >> 3) ^ kswz<HD>(r)) + 2 * (col & 7);
     }
 
-  // key tiles holding a key some row of this tile may attend
+  // key tiles holding a key some row of the workgroup may attend
   const KeyRange kr{Sk, p.causal, p.win};
-  const int k_lo = kr.lo(m0), k_hi = kr.hi(min(m0 + BM, Sq) - 1);
+  const int k_lo = kr.lo(m0), k_hi = kr.hi(min(m0 + RPH, Sq) - 1);
   const int j_begin = k_lo / BN;
   const int j_end = k_hi >= k_lo ? k_hi / BN + 1 : j_begin;
 
   // The dS fragments of a row block exist (were written by the dK/dV kernel) where the block
   // sees some key of the key block; the others are never written and read as zeros here.
-  // This lane's row block (2 w + sub of the tile) sees keys [v_lo, v_hi]; rows past Sq carry
-  // nothing (their dQ is not stored), so their block is left empty.
+  // This lane's row block (2 w + sub of the workgroup) sees keys [v_lo, v_hi]; rows past Sq
+  // carry nothing (their dQ is not stored), so their block is left empty.
   const int rb0 = mw0 + 16 * sub;
   const int v_lo = rb0 < Sq ? kr.lo(rb0) : 1;
   const int v_hi = rb0 < Sq ? kr.hi(min(rb0 + 15, Sq - 1)) : 0;
 
-  // Loads: the K tile through buffer loads (keys past Sk read as zeros), and wave w's dS
-  // fragments (its two row blocks x the step's key blocks) from the (b, hq) slab.  The
-  // prefetches issued past the last step land in stages nothing reads any more (their
-  // offsets stay inside the slab or read zeros past it).
-  TileDma<T, HD, BN> kdma;
-  kdma.init(w, lane);
+  // Loads: the K tile through buffer loads (keys past Sk read as zeros), spread over the
+  // waves, and each wave's own dS fragments (its two row blocks x the step's two key blocks)
+  // from the slab of its head.  The prefetches issued past the last step land in stages
+  // nothing reads any more (their offsets read zeros past the tensor or the slab).
   const rsrc_t rk = make_rsrc(Kg, (unsigned)((size_t)Sk * HD * sizeof(T)));
   const rsrc_t rds = make_rsrc((const char*)p.ds + (size_t)(b * p.H + hq) * p.ds_slab, p.ds_slab);
-  constexpr unsigned TILEB = BN * HD * sizeof(T);  // source bytes of one key tile
-  const unsigned ds_row = (unsigned)(it * p.ds_nk32) * 8u + 2u * w;  // in fragments
+  unsigned k_src[C::KMAX];  // this lane's source offset in the K tile, per instruction
+#pragma unroll
+  for (int k = 0; k < C::KMAX; ++k) {
+    const int gidx = 64 * (w + NW * k) + lane;  // granule of the tile image
+    const int r = gidx / C::CPR, slot = gidx % C::CPR;
+    k_src[k] = (unsigned)(r * C::ROWB + 16 * (slot ^ kswz<HD>(r)));
+  }
+  const unsigned ds_row = (unsigned)((mw0 >> 7) * p.ds_nk32) * 8u + (unsigned)((mw0 >> 4) & 7);
   auto issue_part = [&](int j, char* buf, int k) {
-    if (k < C::KMAX) kdma.issue(k, buf + C::DSB, rk, (unsigned)j * TILEB, spare, lane);
-    if (k < C::NDS) {
-      const int rbw = k % 2, kb = k / 2;
-      b2lds16<FAB_DS_LOAD_AUX>(rds, 16u * lane, (ds_row + (unsigned)(NKB * j + kb) * 8u + rbw) * 1024u,
+    if (k < C::KMAX) {
+      const int q = w + NW * k;
+      char* dst = (!C::kSpare || q < C::KNI) ? buf + C::DSB + 1024 * q : spare;
+      b2lds16(rk, k_src[k], (unsigned)j * C::KT, dst);
+    }
+    if (k < 4) {
+      const int rbw = k & 1, kb = k >> 1;
+      b2lds16<FAB_DS_LOAD_AUX>(rds, 16u * lane, (ds_row + (unsigned)(2 * j + kb) * 8u + rbw) * 1024u,
                                buf + (2 * w + rbw) * C::RB + kb * C::FRAG);
     }
   };
-  constexpr int NPART = C::KMAX > C::NDS ? C::KMAX : C::NDS;
+  constexpr int NPART = C::KMAX > 4 ? C::KMAX : 4;
 #pragma unroll
   for (int st = 0; st < STAGES - 1; ++st)
 #pragma unroll
@@ -942,20 +973,20 @@ __global__ __launch_bounds__(256, WGS) void bwd_dq_ds16_kernel(const BwdParams p
     // Steps where some row of the wave may not see some key read the validity of each dS
     // fragment; elsewhere every fragment was written.
     const bool edge = kr.hi(mw0) < n0 + BN - 1 || kr.lo(mw0 + 31) > n0;
-    bool valid[NKB];
+    bool valid[2];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
       const int key0 = n0 + 32 * kb;
       valid[kb] = v_lo <= v_hi && key0 <= v_hi && key0 + 31 >= v_lo;
     }
     int part = 0;
 #pragma unroll
-    for (int sl = 0; sl < 2 * NKB; ++sl) {
+    for (int sl = 0; sl < 4; ++sl) {
       const int kb = sl >> 1, ks = sl & 1;
       const int so = kb * C::FRAG + ks * 512;  // slice offset in a row block
       F a = lds_frag_tr<T>(cur, ds_off + so, ds_off + so + 128);
       if (edge && !valid[kb]) a = zero8<T>();
-      const int ro = L::rows(16 * sl);
+      const int ro = 16 * sl * C::ROWB;
       F bk = lds_frag_tr<T>(cur, k_off[0][0] + ro, k_off[0][1] + ro);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
@@ -1059,25 +1090,14 @@ static hipError_t go_dq(const BwdParams& p, hipStream_t s, LaunchInfo* info) {
   return hipGetLastError();
 }
 
-// Key blocks per step of the stored-dS dQ kernel and its workgroups per CU (the stage ring
-// fills the LDS share of one workgroup).  Measured at B=2, H=32, S=4096, D=128: 64-key steps
-// with two workgroups per CU (two stages each) 0.246 ms; one workgroup with four stages 0.267;
-// 32-key steps 0.255 (two workgroups, four stages) and 0.280 (one, eight stages).
-#ifndef FAB_DQDS_NKB
-#define FAB_DQDS_NKB 2
-#endif
-#ifndef FAB_DQDS_WGS
-#define FAB_DQDS_WGS 2
-#endif
-
 template <class T, int HD>
 static hipError_t go_dq_ds(const BwdParams& p, hipStream_t s, LaunchInfo* info) {
-  constexpr int NKB = FAB_DQDS_NKB, WGS = HD == 256 ? 1 : FAB_DQDS_WGS;
-  typedef DqDs16<HD, NKB, WGS> C;
-  const int n_qt = (p.Sq + C::BM - 1) / C::BM;
-  const int grid = p.n_units * (p.H / p.H_kv) * n_qt;
-  if (info) *info = LaunchInfo{"bwd_dq_ds16", grid, 256, C::LDS};
-  hipLaunchKernelGGL((bwd_dq_ds16_kernel<T, HD, NKB, WGS>), dim3(grid), dim3(256), 0, s, p);
+  typedef DqDs16<HD> C;
+  const int G = p.H / p.H_kv, NH = (G & 1) ? 1 : 2;
+  const int n_qt = (p.Sq + C::ROWS / NH - 1) / (C::ROWS / NH);
+  const int grid = p.n_units * (G / NH) * n_qt;
+  if (info) *info = LaunchInfo{"bwd_dq_ds16", grid, 64 * C::NW, C::LDS};
+  hipLaunchKernelGGL((bwd_dq_ds16_kernel<T, HD>), dim3(grid), dim3(64 * C::NW), 0, s, p);
   return hipGetLastError();
 }
 
