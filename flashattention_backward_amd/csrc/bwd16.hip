@@ -70,8 +70,10 @@ struct Dkdv16 {
   static constexpr int RED = QH > 1 ? 2 * 64 * HD * 4 : 0;  // epilogue: partial dK or dV exchange
   static constexpr int OROW = HD * 2 + 16;     // epilogue: row pitch of the 16-bit output tile
   static constexpr int OUT = BN * OROW;        // epilogue: the tile's output rows
-  // Loads each wave issues per stage (Q and dO; wave 0 adds the statistics).
+  // Loads each wave issues per stage (Q and dO; wave 0 adds the statistics), and the dS
+  // fragments it stores per step when dS is stored.
   static constexpr int ISSUE = 2 * KMAX;
+  static constexpr int DS_STORES = 2 * KB;
   static_assert(RED + OUT <= LDS, "reduction and output tiles must fit in the staging buffers");
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(TILE % 16 == 0 && VT % 16 == 0, "granule alignment");
@@ -241,23 +243,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   // MFMAs run, so a step starts with them in registers.
   F aq[NC];
   float l2[16], dl[16];
-  // dS of the current step (16-bit, the A operand of dK += dS^T Q), kept until the next step
-  // has stored it when dS is stored; ds_soff is its offset in the group's slabs.
-  F da[KB][2];
-  unsigned ds_soff = 0;
-  bool ds_pending = false;
-  auto store_pending_ds = [&]() {
-    if (store_ds && ds_pending) {
-#pragma unroll
-      for (int nb = 0; nb < KB; ++nb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, da[nb][ks]), rds, ds_voff,
-                                                 ds_soff + (unsigned)(nb * 8192 + ks * 1024),
-                                                 FAB_DS_STORE_AUX);
-    }
-    ds_pending = true;
-  };
+
   auto load_step_operands = [&](const char* __restrict__ buf) {
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) aq[cc] = lds_frag<T>(buf, a_off[cc]);
@@ -284,14 +270,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
     unsigned pq_soff, pst_soff;
     next_offsets(pq_soff, pst_soff);
     const int mw0 = m0 + 32 * qh;
-    // The dS fragments of the previous step go out first, before this step's prefetch: the
-    // end-of-step wait counts the loads issued after the next stage's, and with the stores
-    // issued ahead of them it covers stores a whole step old and nothing of the prefetch,
-    // whether or not stores complete in order with loads.
-    store_pending_ds();
     // dS fragment (nb, ks) of this step: row block mw0 / 16 + ks, key block k32w + nb.
-    ds_soff = (unsigned)hh * p.ds_slab +
-              (unsigned)((((mw0 >> 7) * p.ds_nk32 + k32w) * 8 + ((mw0 >> 4) & 7)) * 1024);
+    const unsigned ds_soff = (unsigned)hh * p.ds_slab +
+                             (unsigned)((((mw0 >> 7) * p.ds_nk32 + k32w) * 8 + ((mw0 >> 4) & 7)) * 1024);
 
     // ---- S = Q K^T for the wave's key blocks; the prefetch is spread over it, one instruction
     // per head-dim slice, so the wave never stalls on a burst of loads.
@@ -345,7 +326,17 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
     // many as their issue time covers (an exponential with its fma and conversion takes about
     // two thirds of an MFMA's), and never fewer than registers 0..7; the rest run under the
     // dK MFMAs of rows 0..15, which otherwise leave the vector ALU idle.
-    F pa[KB][2];
+    F pa[KB][2], da[KB][2];
+    // The dS fragments of rows 16 ks .. 16 ks + 15 go out as soon as they are formed.
+    auto store_ds_rows = [&](int ks) {
+      if (store_ds) {
+#pragma unroll
+        for (int nb = 0; nb < KB; ++nb)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, da[nb][ks]), rds, ds_voff,
+                                                 ds_soff + (unsigned)(nb * 8192 + ks * 1024),
+                                                 FAB_DS_STORE_AUX);
+      }
+    };
     constexpr int NE = 16 * KB;
     constexpr int NE_FIT = NC * KB * 3 / 2;
     constexpr int NE_DP = NE < NE_FIT ? NE : (NE_FIT > 8 * KB ? NE_FIT : 8 * KB);
@@ -407,6 +398,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    store_ds_rows(0);
     // ---- dK += dS^T Q, rows 0..15, with the remaining exponentials formed meanwhile.
     constexpr int NR = NE - NE_DP;
     constexpr int PER_MMA_E = (NR + NDB * KB - 1) / (NDB * KB);
@@ -442,9 +434,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    store_ds_rows(1);
     // ---- end of the step for the workgroup: the next stage has landed (the loads of the one
-    // after it may stay in flight) and no wave reads `cur` any more.
-    wait_vm_le<C::ISSUE * (STAGES - 2)>();
+    // after it may stay in flight) and no wave reads `cur` any more.  Vector memory operations
+    // retire in issue order, stores among loads, so the wait names how many were issued after
+    // the next stage's loads: the prefetch issued in this step and, with stored dS, the stores
+    // of the previous step and of this one, which then have two steps to retire.
+    if (store_ds) wait_vm_le<C::ISSUE * (STAGES - 2) + C::DS_STORES * (STAGES - 1)>();
+    else wait_vm_le<C::ISSUE * (STAGES - 2)>();
     barrier_lds();
     load_step_operands(nb1);
     // ---- dK += dS^T Q for rows 16..31 while the next step's operands arrive.
@@ -471,7 +468,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
       --it;
     }
   }
-  store_pending_ds();  // the last step's dS
   // the epilogue reuses the staging buffers: every prefetch must have landed
   wait_vm_all();
   barrier_lds();
