@@ -48,7 +48,7 @@ CSRC = os.path.join(ROOT, "flashattention_backward_amd", "csrc")
 # dQ where it recomputes dS.
 KERNEL_CONTRACTIONS = {"stored_ds": {"bwd_dkdv": 4, "bwd_dq": 1},
                        "recompute": {"bwd_dkdv": 4, "bwd_dq": 3}}
-MODES = ("stored_ds", "recompute")
+MODES = ("best", "stored_ds", "recompute")
 KERNEL_SOURCE = {"bwd_dkdv": "bwd16.hip", "bwd_dq": "bwd16.hip", "preprocess": "preprocess.hip"}
 
 
@@ -156,7 +156,7 @@ def cpu_baseline(w, q, k, v, do, max_groups=None):
 class Bwd:
     """Preallocated buffers and raw C-ABI calls for one workload (no allocation per step)."""
 
-    def __init__(self, w, q, k, v, do, mode="stored_ds"):
+    def __init__(self, w, q, k, v, do, mode="best"):
         import torch
 
         import flashattention_backward_amd as fab
@@ -169,10 +169,10 @@ class Bwd:
         self.dk = torch.empty_like(self.k)
         self.dv = torch.empty_like(self.v)
         self.code = fab.DTYPE_CODES[str(self.q.dtype).replace("torch.", "")]
-        # the workspace size selects the mode; the stored-dS size falls back to the recompute
-        # size where that mode does not apply (float32, very large dS buffers)
+        # the workspace size selects the mode: the library's recommendation ("best"), or one
+        # forced (the stored-dS size falls back to the recompute size where that mode cannot run)
         nb = fab.bwd_workspace_bytes(w.B, w.H, w.H_kv, w.Sq, w.Sk, w.D, self.code,
-                                     store_ds=(mode == "stored_ds"))
+                                     store_ds={"best": None, "stored_ds": True, "recompute": False}[mode])
         nmin = fab.bwd_workspace_bytes(w.B, w.H, w.H_kv, w.Sq, w.Sk, w.D, self.code, store_ds=False)
         self.mode = "stored_ds" if nb > nmin else "recompute"
         self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
@@ -270,7 +270,7 @@ def call_stats(ms):
             "p90": round(pct(0.9), 4)}
 
 
-def bench_workload(w, steps, warmup, with_cpu, inputs=None, mode="stored_ds"):
+def bench_workload(w, steps, warmup, with_cpu, inputs=None, mode="best"):
     import torch
     q, k, v, do = inputs if inputs is not None else workloads.make_inputs(w)
     cpu = cpu_baseline(w, q, k, v, do) if with_cpu else None
@@ -351,7 +351,7 @@ def bench_workload(w, steps, warmup, with_cpu, inputs=None, mode="stored_ds"):
     return line
 
 
-def only_mode(w, what, steps, warmup, mode="stored_ds"):
+def only_mode(w, what, steps, warmup, mode="best"):
     """A bare launch loop for rocprofv3 (no timing, no CPU baseline)."""
     import torch
     if what == "copy":
@@ -386,9 +386,9 @@ def main():
     ap.add_argument("--all", action="store_true", help="one JSON line per named workload (no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["bwd", "dkdv", "dq", "preprocess", "fwd", "copy"])
-    ap.add_argument("--mode", choices=MODES, default="stored_ds",
-                    help="how dQ is formed: from the dS the dK/dV kernel stores (default, where it "
-                         "applies) or by recomputing S and dP")
+    ap.add_argument("--mode", choices=MODES, default="best",
+                    help="how dQ is formed: the library's recommendation for the workload (default), "
+                         "from the dS the dK/dV kernel stores, or by recomputing S and dP")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
             L.fab_bwd_workspace_bytes.argtypes = [i] * 7
             L.fab_bwd_workspace_bytes_min.restype = sz
             L.fab_bwd_workspace_bytes_min.argtypes = [i] * 7
+            L.fab_bwd_workspace_bytes_ds.restype = sz
+            L.fab_bwd_workspace_bytes_ds.argtypes = [i] * 7
             L.fab_fwd.restype = i
             L.fab_fwd.argtypes = [vp] * 5 + [i] * 7 + [i, i, f, vp]
             L.fab_bwd_preprocess.restype = i
@@ -105,11 +107,18 @@ def _check_tensor(t, name, shape, dtype, device):
     _require(t.is_contiguous(), name, "must be contiguous")
 
 
-def bwd_workspace_bytes(B, H, H_kv, Sq, Sk, D, dtype_code, store_ds: bool = True) -> int:
-    """Workspace bytes for the fastest mode (store_ds=True: stored dS where it applies) or the
-    least fab_bwd accepts (store_ds=False: dQ recomputes dS)."""
-    f = lib().fab_bwd_workspace_bytes if store_ds else lib().fab_bwd_workspace_bytes_min
-    return int(f(B, H, H_kv, Sq, Sk, D, dtype_code))
+def bwd_workspace_bytes(B, H, H_kv, Sq, Sk, D, dtype_code, store_ds: bool | None = None) -> int:
+    """Workspace bytes that select a mode of the backward: the recommended one (store_ds=None),
+    stored dS (True; where that mode cannot run, the recompute size) or recompute (False)."""
+    L = lib()
+    args = (B, H, H_kv, Sq, Sk, D, dtype_code)
+    if store_ds is None:
+        return int(L.fab_bwd_workspace_bytes(*args))
+    if store_ds:
+        n = int(L.fab_bwd_workspace_bytes_ds(*args))
+        if n:
+            return n
+    return int(L.fab_bwd_workspace_bytes_min(*args))
 
 
 def _window(window_size) -> int:
@@ -167,11 +176,11 @@ def bwd_preprocess(do, o, lse):
 
 def bwd(do, q, k, v, o, lse, num_heads: int | None = None, num_kv_heads: int | None = None,
         causal: bool = False, scale: float | None = None, workspace=None, window_size: int = 0,
-        store_ds: bool = True):
+        store_ds: bool | None = None):
     """The backward: returns (dq, dk, dv) with the shapes and dtype of (q, k, v).  `causal`,
     `scale` and `window_size` must be those the forward ran with.  Without a `workspace`, one is
-    allocated for the stored-dS mode (store_ds=True, where it applies) or for the recompute
-    mode (store_ds=False); a given workspace selects the mode by its size."""
+    allocated for the recommended mode (store_ds=None), the stored-dS mode (True, where it can
+    run) or the recompute mode (False); a given workspace selects the mode by its size."""
     import torch
     _require(q.dim() == 4, "q", f"must be 4-D [B, H, Sq, D], got {tuple(q.shape)}")
     _require(k.dim() == 4, "k", f"must be 4-D [B, H_kv, Sk, D], got {tuple(k.shape)}")

@@ -208,6 +208,18 @@ void set_ds(fab::BwdParams& p, const void* workspace) {
   p.ds_nk32 = (int)(fab::ds_keys(p.Sk) / 32);
 }
 
+// The mode fab_bwd_workspace_bytes recommends: stored dS where it applies, measured faster
+// from head dim 96 up (it moves 2 bytes of dS per allowed pair to save 4 D FLOPs of recompute,
+// which below D = 96 cost less than the traffic), and not for problems small enough for the
+// single fused launch of the recomputing kernels.
+bool recommend_ds(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype) {
+  if (D < 96 || !ds_mode_fits(B, H, H_kv, Sq, Sk, dtype)) return false;
+  const fab::BwdParams p =
+      bwd_params(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                 B, H, H_kv, Sq, Sk, 0, 0, 1.f);
+  return !fab::bwd_small16_fits(p, D);
+}
+
 // Checks shared by fab_bwd and the two step-2 entry points (every pointer but dq/dk/dv).
 fab_status check_bwd_inputs(const void* dO, const void* q, const void* k, const void* v,
                             int B, int H, int H_kv, int Sq, int Sk, int D, int dtype,
@@ -315,6 +327,16 @@ fab_status run_bwd(const void* dO, const void* q, const void* k, const void* v, 
     log_launch(li);
     return FAB_OK;
   }
+  if (tiled(dtype) && fab::bwd_small16_fits(p, D)) {
+    // A small problem: step 1, then both step-2 kernels in one launch, which fills the device
+    // where each grid alone would leave it half idle.
+    const fab::PreParams pp = pre_params(dO, o, lse, workspace, B, H, Sq);
+    FAB_TRY(launched(fab::launch_preprocess(pp, dtype, D, s, &li), "preprocess"));
+    log_launch(li);
+    FAB_TRY(launched(fab::launch_bwd_small16(p, dtype, D, s, &li), "bwd_small"));
+    log_launch(li);
+    return FAB_OK;
+  }
   if (tiled(dtype)) {
     // Step 1 runs inside the dQ kernel, which therefore goes first: it writes the row
     // statistics the dK/dV kernel then reads from the workspace.
@@ -345,7 +367,15 @@ size_t fab_bwd_workspace_bytes(int B, int H, int H_kv, int Sq, int Sk, int D, in
   fab_status s = check_common(B, H, H_kv, Sq, Sk, D, dtype);
   g_last_error = saved;
   if (s != FAB_OK) return 0;
-  return ds_mode_fits(B, H, H_kv, Sq, Sk, dtype) ? ws_bytes_ds(B, H, Sq, Sk) : ws_bytes(B, H, Sq);
+  return recommend_ds(B, H, H_kv, Sq, Sk, D, dtype) ? ws_bytes_ds(B, H, Sq, Sk) : ws_bytes(B, H, Sq);
+}
+
+size_t fab_bwd_workspace_bytes_ds(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype) {
+  std::string saved = g_last_error;
+  fab_status s = check_common(B, H, H_kv, Sq, Sk, D, dtype);
+  g_last_error = saved;
+  if (s != FAB_OK || !ds_mode_fits(B, H, H_kv, Sq, Sk, dtype)) return 0;
+  return ws_bytes_ds(B, H, Sq, Sk);
 }
 
 size_t fab_bwd_workspace_bytes_min(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype) {

@@ -79,8 +79,10 @@ struct Dkdv16 {
   static_assert(TILE % 16 == 0 && VT % 16 == 0, "granule alignment");
 };
 
+// The kernel body, for workgroup `wg` of the launch, with C::LDS bytes of LDS at `smem`
+// (1024-byte aligned); the kernels below run it on their own or beside the dQ body.
 template <class T, int HD, bool WIDE>
-__global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
+__device__ __forceinline__ void dkdv16_body(const BwdParams& p, int wg, char* smem) {
   typedef Dkdv16<HD, WIDE> C;
   typedef typename Frag<T>::type F;
   typedef TileDma<T, HD, C::BM> Dma;
@@ -90,7 +92,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   typedef typename C::L L;
   constexpr unsigned ROWB = HD * sizeof(T);
 
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
   char* const vtile = smem + C::STAGES * C::BUF;
   char* const spare = vtile + C::VT;  // only used when the tile DMA needs padding loads
 
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   const int lane = tid & 63, hl = lane >> 5, c32 = lane & 31;
   const int kb = w % C::KG, qh = w / C::KG;
 
-  const WorkItem wi = map_work(blockIdx.x, p.n_units, p.units_per_xcd);
+  const WorkItem wi = map_work(wg, p.n_units, p.units_per_xcd);
   const int b = wi.unit / p.H_kv, g = wi.unit % p.H_kv;
   const int n0 = wi.step * BN;
   const int G = p.H / p.H_kv;
@@ -546,6 +547,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
   }
 }
 
+template <class T, int HD, bool WIDE>
+__global__ __launch_bounds__(256) void bwd_dkdv16_kernel(const BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[Dkdv16<HD, WIDE>::LDS];
+  dkdv16_body<T, HD, WIDE>(p, blockIdx.x, smem);
+}
+
 // =======================================================================================
 // dQ: query-tile outer.  A workgroup owns BM = 128 query rows of one (batch, head); wave w
 // owns 32 of them, with their Q and dO fragments, LSE and D in registers (one query row per
@@ -576,7 +583,7 @@ struct Dq16 {
 };
 
 template <class T, int HD, int NB>
-__global__ __launch_bounds__(256, (HD <= 128 ? 2 : 1)) void bwd_dq16_kernel(const BwdParams p) {
+__device__ __forceinline__ void dq16_body(const BwdParams& p, int wg, char* smem) {
   typedef Dq16<HD, NB> C;
   typedef typename Frag<T>::type F;
   constexpr int NC = HD / 16, NDB = HD / 32;
@@ -584,7 +591,6 @@ __global__ __launch_bounds__(256, (HD <= 128 ? 2 : 1)) void bwd_dq16_kernel(cons
   constexpr int BM = C::BM, BN = C::BN, STAGES = C::STAGES;
   typedef typename C::L L;
 
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
   char* const spare = smem + C::STAGES * C::BUF;
 
   const int tid = threadIdx.x;
@@ -595,7 +601,7 @@ __global__ __launch_bounds__(256, (HD <= 128 ? 2 : 1)) void bwd_dq16_kernel(cons
   const int G = p.H / p.H_kv;
   const int n_qt = (Sq + BM - 1) / BM;
 
-  const WorkItem wi = map_work(blockIdx.x, p.n_units, p.units_per_xcd);
+  const WorkItem wi = map_work(wg, p.n_units, p.units_per_xcd);
   const int b = wi.unit / p.H_kv, g = wi.unit % p.H_kv;
   const int hq = g * G + wi.step % G;
   const int tq = wi.step / G;
@@ -798,6 +804,40 @@ __global__ __launch_bounds__(256, (HD <= 128 ? 2 : 1)) void bwd_dq16_kernel(cons
     typedef T v8 __attribute__((ext_vector_type(8)));
     const v8 val = *reinterpret_cast<const v8*>(otile + row * C::OROW + 16 * ch);
     if (mw0 + row < Sq) *reinterpret_cast<v8*>(dQg + (size_t)(mw0 + row) * HD + 8 * ch) = val;
+  }
+}
+
+template <class T, int HD, int NB>
+__global__ __launch_bounds__(256, (HD <= 128 ? 2 : 1)) void bwd_dq16_kernel(const BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[Dq16<HD, NB>::LDS];
+  dq16_body<T, HD, NB>(p, blockIdx.x, smem);
+}
+
+// Key blocks of 32 per step of the dQ kernel (1: 32-key steps through a three-stage ring;
+// 2: 64-key steps through a double buffer, which pays the per-step barrier, waits and
+// scalar bookkeeping half as often and measures 2% faster at head dim 128).
+#ifndef FAB_DQ_NB
+#define FAB_DQ_NB 2
+#endif
+constexpr int kDqNB = FAB_DQ_NB;
+
+// =======================================================================================
+// Both recomputing step-2 kernels in one launch, for problems whose two grids together fit
+// the device in one round: the first n_dkdv workgroups (rounded up to a multiple of the 8
+// XCDs, so that the dQ workgroups keep the XCD order of their own grid; the padding ones
+// exit at once) run the dK/dV body with 128-key tiles, the rest the dQ body.  Separate
+// launches would leave half the device idle in each; here both halves run at once.  The
+// row statistics come from a preprocess launch before it.
+// =======================================================================================
+template <class T, int HD>
+__global__ __launch_bounds__(256) void bwd_small16_kernel(const BwdParams p, int n_dkdv, int n_dkdv_pad) {
+  constexpr int L1 = Dkdv16<HD, false>::LDS, L2 = Dq16<HD, kDqNB>::LDS;
+  __shared__ __attribute__((aligned(1024))) char smem[L1 > L2 ? L1 : L2];
+  const int wg = blockIdx.x;
+  if (wg < n_dkdv_pad) {
+    if (wg < n_dkdv) dkdv16_body<T, HD, false>(p, wg, smem);
+  } else {
+    dq16_body<T, HD, kDqNB>(p, wg - n_dkdv_pad, smem);
   }
 }
 
@@ -1068,14 +1108,6 @@ static hipError_t go_dkdv(const BwdParams& p, hipStream_t s, LaunchInfo* info) {
   return go_dkdv_cfg<T, HD, false>(p, s, info);
 }
 
-// Key blocks of 32 per step of the dQ kernel (1: 32-key steps through a three-stage ring;
-// 2: 64-key steps through a double buffer, which pays the per-step barrier, waits and
-// scalar bookkeeping half as often and measures 2% faster at head dim 128).
-#ifndef FAB_DQ_NB
-#define FAB_DQ_NB 2
-#endif
-constexpr int kDqNB = FAB_DQ_NB;
-
 template <class T, int HD>
 static hipError_t go_dq(const BwdParams& p, hipStream_t s, LaunchInfo* info) {
   typedef Dq16<HD, kDqNB> C;
@@ -1128,6 +1160,47 @@ static hipError_t dq_hd(const BwdParams& p, int hd, hipStream_t s, LaunchInfo* i
     case 128: return go_dq<T, 128>(p, s, info);
     default: return go_dq<T, 256>(p, s, info);
   }
+}
+
+// Workgroups of the two recomputing step-2 kernels when they share one launch (128-key dK/dV
+// tiles, the dK/dV count rounded up to whole rounds of the XCDs) and whether that launch fits
+// the device in one round.
+static void small_counts(const BwdParams& p, int hd, int& n_dkdv, int& n_dkdv_pad, int& n_dq) {
+  const int bn = hd == 256 ? Dkdv16<256, false>::BN : Dkdv16<128, false>::BN;
+  n_dkdv = p.n_units * ((p.Sk + bn - 1) / bn);
+  n_dkdv_pad = (n_dkdv + 7) / 8 * 8;
+  n_dq = p.n_units * (p.H / p.H_kv) * ((p.Sq + 127) / 128);
+}
+
+bool bwd_small16_fits(const BwdParams& p, int hd) {
+  int n_dkdv, n_pad, n_dq;
+  small_counts(p, hd, n_dkdv, n_pad, n_dq);
+  return (long long)n_pad + n_dq <= device_cus();
+}
+
+template <class T, int HD>
+static hipError_t go_small(const BwdParams& p, hipStream_t s, LaunchInfo* info) {
+  int n_dkdv, n_pad, n_dq;
+  small_counts(p, HD, n_dkdv, n_pad, n_dq);
+  constexpr int L1 = Dkdv16<HD, false>::LDS, L2 = Dq16<HD, kDqNB>::LDS;
+  if (info) *info = LaunchInfo{"bwd_small16", n_pad + n_dq, 256, L1 > L2 ? L1 : L2};
+  hipLaunchKernelGGL((bwd_small16_kernel<T, HD>), dim3(n_pad + n_dq), dim3(256), 0, s, p, n_dkdv, n_pad);
+  return hipGetLastError();
+}
+
+template <class T>
+static hipError_t small_hd(const BwdParams& p, int hd, hipStream_t s, LaunchInfo* info) {
+  switch (hd) {
+    case 32: return go_small<T, 32>(p, s, info);
+    case 64: return go_small<T, 64>(p, s, info);
+    case 96: return go_small<T, 96>(p, s, info);
+    case 128: return go_small<T, 128>(p, s, info);
+    default: return go_small<T, 256>(p, s, info);
+  }
+}
+
+hipError_t launch_bwd_small16(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info) {
+  return dt == kBF16 ? small_hd<bf16>(p, hd, s, info) : small_hd<f16>(p, hd, s, info);
 }
 
 hipError_t launch_bwd_dkdv16(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info) {

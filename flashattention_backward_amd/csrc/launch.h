@@ -89,6 +89,10 @@ hipError_t launch_bwd_dkdv(const BwdParams& p, int dt, int hd, hipStream_t s, La
 hipError_t launch_bwd_dq(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info);
 hipError_t launch_bwd_dkdv16(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info);
 hipError_t launch_bwd_dq16(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info);
+// Both recomputing step-2 kernels in one launch (row statistics from a preprocess first), and
+// whether the problem is small enough for it (the two grids together fit the device at once).
+bool bwd_small16_fits(const BwdParams& p, int hd);
+hipError_t launch_bwd_small16(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info);
 // dQ = scale * dS K from the dS fragments the dK/dV kernel stored (p.ds set).
 hipError_t launch_bwd_dq_ds16(const BwdParams& p, int dt, int hd, hipStream_t s, LaunchInfo* info);
 

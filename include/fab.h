@@ -74,15 +74,18 @@ const char* fab_version(void);
 const char* fab_last_error(void);
 
 /*
- * Bytes of device workspace for the fastest mode of the backward at these sizes (0 if the
- * sizes are invalid); fab_bwd_workspace_bytes_min gives the least fab_bwd accepts.
+ * Bytes of device workspace for the recommended mode of the backward at these sizes (0 if the
+ * sizes are invalid); fab_bwd_workspace_bytes_min gives the least fab_bwd accepts (the
+ * recompute mode) and fab_bwd_workspace_bytes_ds the size that selects the stored-dS mode (0
+ * where that mode cannot run: float32, or a dS buffer past the limits below).
  *
- * The workspace selects how dQ is formed.  With at least fab_bwd_workspace_bytes bytes, for
- * float16 / bfloat16 inputs whose dS buffer fits (below), the dK/dV kernel also stores every
- * dS value it forms and dQ = scale * dS K reads them back ("stored dS": 10 D FLOPs per allowed
- * pair instead of 14 D, for 2 bytes of HBM written and read per pair).  With less (at least
- * fab_bwd_workspace_bytes_min), or for float32, dQ recomputes S and dP ("recompute").  Both
- * give the same result up to float rounding order; each is deterministic.
+ * The workspace selects how dQ is formed.  With at least fab_bwd_workspace_bytes_ds bytes the
+ * dK/dV kernel also stores every dS value it forms and dQ = scale * dS K reads them back
+ * ("stored dS": 10 D FLOPs per allowed pair instead of 14 D, for 2 bytes of HBM written and
+ * read per pair).  With less (at least fab_bwd_workspace_bytes_min), or for float32, dQ
+ * recomputes S and dP ("recompute").  Both give the same result up to float rounding order;
+ * each is deterministic.  The recommended mode is stored dS from head dim 96 up, except for
+ * problems so small that the two recomputing kernels run in one launch.
  *
  * Layout.  From byte 0, as written by the preprocessing step, float32 pairs
  *   ws[((b * H + h) * Sq_pad + i) * 2 + 0] = lse[b, h, i] * log2(e)
@@ -99,6 +102,7 @@ const char* fab_last_error(void);
  */
 size_t fab_bwd_workspace_bytes(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype);
 size_t fab_bwd_workspace_bytes_min(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype);
+size_t fab_bwd_workspace_bytes_ds(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype);
 
 /*
  * Supporting forward (boostr autograd_attention.rs, var_flash_attention: the forward
@@ -141,7 +145,8 @@ fab_status fab_bwd_preprocess(const void* dO, const void* o, const float* lse,
  * Deterministic: no atomics, identical inputs and workspace size give bitwise identical
  * outputs.  Launches: stored dS -- step 1, the dK/dV kernel (which also writes dS), then
  * dQ = scale * dS K; recompute (16-bit) -- the dQ kernel (with step 1 folded into its
- * prologue), then the dK/dV kernel; float32 -- step 1, dK/dV, dQ.
+ * prologue), then the dK/dV kernel, or, where both grids together fit the device at once,
+ * step 1 and then both kernels in one launch; float32 -- step 1, dK/dV, dQ.
  */
 fab_status fab_bwd(const void* dO, const void* q, const void* k, const void* v,
                    const void* o, const float* lse, void* dq, void* dk, void* dv,

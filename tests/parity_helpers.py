@@ -65,9 +65,10 @@ def window_span_ranges(c: int, e: int, S: int, W: int):
     return (lo, e), (lo, e - W + 1 if e < S else S)
 
 
-def run_gpu(fab, q, k, v, do, causal, scale, window=0, store_ds=True):
+def run_gpu(fab, q, k, v, do, causal, scale, window=0, store_ds=None):
     """End-to-end HIP path: fwd then bwd, all inputs resident on cuda:0.  store_ds selects the
-    backward's mode through its workspace size (stored dS where it applies, else recompute)."""
+    backward's mode through its workspace size: None the recommended one, True stored dS
+    (where it can run), False recompute."""
     import torch
     dev = torch.device("cuda:0")
     qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
@@ -79,12 +80,12 @@ def run_gpu(fab, q, k, v, do, causal, scale, window=0, store_ds=True):
 
 
 def check_end_to_end(fab, w: workloads.Workload, groups=None, jobs: int = 1, check_fwd=True,
-                     store_ds=True):
+                     store_ds=None):
     """GPU fwd+bwd against oracle fwd+bwd on the same rounded inputs.  With ``groups`` only
     those (b, kv head) groups are compared (full-size runs)."""
     say(f"[case] {w.name} dtype={w.dtype} B={w.B} H={w.H} H_kv={w.H_kv} Sq={w.Sq} Sk={w.Sk} "
         f"D={w.D} causal={w.causal} window={w.window} seed={w.seed} groups={groups} "
-        f"mode={'stored-dS' if store_ds else 'recompute'}")
+        f"mode={ {None: 'recommended', True: 'stored-dS', False: 'recompute'}[store_ds] }")
     q, k, v, do = workloads.make_inputs(w)
     out = run_gpu(fab, q, k, v, do, w.causal, w.scale, w.window, store_ds=store_ds)
     if groups is None:

@@ -33,12 +33,19 @@ def test_workspace_bytes():
     assert L.fab_bwd_workspace_bytes_min(1, 1, 1, 3, 5, 64, 2) == 512
     # stored dS: the statistics to a 4 KB boundary, then per (b, h) Sq rounded up to 128 times
     # Sk rounded up to 256 16-bit values
-    assert L.fab_bwd_workspace_bytes(2, 32, 8, 4096, 4096, 128, 2) == 2 * 32 * 4096 * 8 + 64 * 4096 * 4096 * 2
-    assert L.fab_bwd_workspace_bytes(1, 3, 1, 130, 300, 64, 1) == 8192 + 3 * 256 * 512 * 2  # 4608 B of statistics
+    assert L.fab_bwd_workspace_bytes_ds(2, 32, 8, 4096, 4096, 128, 2) == 2 * 32 * 4096 * 8 + 64 * 4096 * 4096 * 2
+    assert L.fab_bwd_workspace_bytes_ds(1, 3, 1, 130, 300, 64, 1) == 8192 + 3 * 256 * 512 * 2  # 4608 B of statistics
+    assert L.fab_bwd_workspace_bytes_ds(1, 1, 1, 3, 5, 64, 0) == 0                        # no stored dS in fp32
+    # recommended: stored dS from head dim 96 up, unless both recomputing grids fit one launch
+    assert L.fab_bwd_workspace_bytes(2, 32, 8, 4096, 4096, 128, 2) == L.fab_bwd_workspace_bytes_ds(2, 32, 8, 4096, 4096, 128, 2)
+    assert L.fab_bwd_workspace_bytes(2, 32, 8, 4096, 4096, 96, 2) == L.fab_bwd_workspace_bytes_ds(2, 32, 8, 4096, 4096, 96, 2)
+    assert L.fab_bwd_workspace_bytes(2, 32, 8, 4096, 4096, 64, 2) == L.fab_bwd_workspace_bytes_min(2, 32, 8, 4096, 4096, 64, 2)
+    assert L.fab_bwd_workspace_bytes(1, 8, 2, 300, 300, 128, 2) == L.fab_bwd_workspace_bytes_min(1, 8, 2, 300, 300, 128, 2)
     # float32 has no stored-dS mode; too large a dS buffer (here 64 GiB) falls back as well
     assert L.fab_bwd_workspace_bytes(1, 1, 1, 3, 5, 64, 0) == 512
     assert L.fab_bwd_workspace_bytes(1, 3, 3, 65, 5, 64, 0) == 3 * 128 * 8
-    assert L.fab_bwd_workspace_bytes(1, 2, 2, 131072, 131072, 64, 2) == L.fab_bwd_workspace_bytes_min(1, 2, 2, 131072, 131072, 64, 2)
+    assert L.fab_bwd_workspace_bytes_ds(1, 2, 2, 131072, 131072, 128, 2) == 0  # a 64 GiB dS buffer
+    assert L.fab_bwd_workspace_bytes(1, 2, 2, 131072, 131072, 128, 2) == L.fab_bwd_workspace_bytes_min(1, 2, 2, 131072, 131072, 128, 2)
     assert L.fab_bwd_workspace_bytes(1, 3, 2, 3, 5, 64, 0) == 0    # H % H_kv != 0
     assert L.fab_bwd_workspace_bytes(1, 1, 1, 3, 5, 80, 0) == 0    # head dim
     assert L.fab_bwd_workspace_bytes(1, 1, 1, 3, 5, 256, 0) == 0   # head dim 256 in fp32

@@ -139,7 +139,7 @@ def test_step_entry_points_stored_ds(fab, dt, D, causal, win):
     o, lse = fab.fwd(qd, kd, vd, causal=causal, scale=w.scale, window_size=win)
     L = fab.lib()
     code = fab.DTYPE_CODES[str(qd.dtype).replace("torch.", "")]
-    nb = fab.bwd_workspace_bytes(w.B, w.H, w.H_kv, w.Sq, w.Sk, D, code)
+    nb = fab.bwd_workspace_bytes(w.B, w.H, w.H_kv, w.Sq, w.Sk, D, code, store_ds=True)
     assert nb > fab.bwd_workspace_bytes(w.B, w.H, w.H_kv, w.Sq, w.Sk, D, code, store_ds=False)
     ws = torch.empty(nb, dtype=torch.uint8, device=dev)
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
