@@ -49,7 +49,8 @@ CSRC = os.path.join(ROOT, "flashattention_backward_amd", "csrc")
 KERNEL_CONTRACTIONS = {"stored_ds": {"bwd_dkdv": 4, "bwd_dq": 1},
                        "recompute": {"bwd_dkdv": 4, "bwd_dq": 3}}
 MODES = ("best", "stored_ds", "recompute")
-KERNEL_SOURCE = {"bwd_dkdv": "bwd16.hip", "bwd_dq": "bwd16.hip", "preprocess": "preprocess.hip"}
+KERNEL_SOURCE = {"bwd_dkdv": "bwd16.hip", "bwd_dq": "bwd16.hip", "bwd_dkdv_ds": "bwd16.hip",
+                 "bwd_dq_ds": "bwd16.hip", "preprocess": "preprocess.hip"}
 
 
 def allowed_pairs(w) -> float:
@@ -69,18 +70,23 @@ def source_digest(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken on
-    the current kernel source (same digest); else None."""
-    path = os.path.join(PROFILES, f"{kernel}_{workload}_hbm_traffic.md")
+def recorded_value(kernel: str, workload: str, what: str, key: str):
+    """A figure from a committed rocprofv3 counter summary (profiles/<kernel>_<workload>_<what>.md,
+    line `key: value`), if it was taken on the current kernel source (same digest); else None."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_{what}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     dig = re.search(r"source_digest:\s*([0-9a-f]+)", text)
-    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    val = re.search(key + r":\s*([0-9.eE+-]+)", text)
     if not dig or not val or dig.group(1) != source_digest(kernel):
         return None
     return float(val.group(1))
+
+
+def recorded_traffic(kernel: str, workload: str):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) on the current source."""
+    return recorded_value(kernel, workload, "hbm_traffic", "hbm_bytes_per_launch")
 
 
 # ----------------------------------------------------------------------------- CPU baseline
@@ -175,6 +181,7 @@ class Bwd:
                                      store_ds={"best": None, "stored_ds": True, "recompute": False}[mode])
         nmin = fab.bwd_workspace_bytes(w.B, w.H, w.H_kv, w.Sq, w.Sk, w.D, self.code, store_ds=False)
         self.mode = "stored_ds" if nb > nmin else "recompute"
+        self.plan = fab.bwd_plan(w.B, w.H, w.H_kv, w.Sq, w.Sk, w.D, self.code, nb)
         self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
         self.stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         self.dims = (w.B, w.H, w.H_kv, w.Sq, w.Sk, w.D, self.code, int(w.causal), w.window,
@@ -305,11 +312,40 @@ def bench_workload(w, steps, warmup, with_cpu, inputs=None, mode="best"):
     flops = w.bwd_flops()
     tflops = flops / (ms * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[w.dtype]
+    # the kernels of the path, named by role and mode (in the stored-dS mode the dK/dV kernel
+    # also writes dS and the dQ kernel is the contraction over it)
+    tag = "_ds" if b.mode == "stored_ds" else ""
+    names = {"bwd_dkdv": "bwd_dkdv" + tag, "bwd_dq": "bwd_dq" + tag, "preprocess": "preprocess"}
     dom = max(("bwd_dkdv", "bwd_dq"), key=lambda n: k_ms[n])
     kflops = 2.0 * w.D * KERNEL_CONTRACTIONS[b.mode][dom] * allowed_pairs(w)
     achieved = kflops / (k_ms[dom] * 1e-3) / 1e12
     es = 4 if w.dtype == "fp32" else 2
     pre_bytes = w.B * w.H * w.Sq * (2 * w.D * es + 4 + 8)  # read dO, O, LSE; write {LSE', D}
+    kernels = {}
+    for role in ("bwd_dkdv", "bwd_dq"):
+        kf = 2.0 * w.D * KERNEL_CONTRACTIONS[b.mode][role] * allowed_pairs(w)
+        kernels[names[role]] = {"ms": round(k_ms[role], 4), "bound": "mfma",
+                                "achieved_TFLOPs": round(kf / (k_ms[role] * 1e-3) / 1e12, 2),
+                                "frac_of_peak": round(kf / (k_ms[role] * 1e-3) / 1e12 / peak, 4),
+                                "mfma_busy": recorded_value(names[role], w.name, "counters", "mfma_busy_frac"),
+                                "traffic": recorded_traffic(names[role], w.name)}
+    if b.mode == "stored_ds":
+        # dQ = scale dS K streams dS from HBM: its algorithmic bytes are dS (2 bytes per allowed
+        # pair), K once and dQ once
+        qb = 2.0 * allowed_pairs(w) + (w.B * w.H_kv * w.Sk + w.B * w.H * w.Sq) * w.D * es
+        kd = kernels[names["bwd_dq"]]
+        kd.update({"bound": "hbm", "algorithmic_bytes": qb,
+                   "achieved_GBps": round(qb / (k_ms["bwd_dq"] * 1e-3) / 1e9, 1),
+                   "frac_of_hbm_peak": round(qb / (k_ms["bwd_dq"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+    kernels["preprocess"] = {"ms": round(k_ms["preprocess"], 4), "bound": "hbm", "algorithmic_bytes": pre_bytes,
+                             "achieved_GBps": round(pre_bytes / (k_ms["preprocess"] * 1e-3) / 1e9, 1),
+                             "frac_of_hbm_peak": round(pre_bytes / (k_ms["preprocess"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                             "on_path": b.plan != "recompute",
+                             "traffic": recorded_traffic("preprocess", w.name)}
+    if b.plan == "recompute":
+        # step 1 runs in the dQ kernel's prologue: its cost is what fab_bwd takes beyond the
+        # dK/dV kernel and the dQ kernel without it (one launch gap included)
+        kernels["preprocess"]["fused_in_dq_ms_estimate"] = round(ms - k_ms["bwd_dkdv"] - k_ms["bwd_dq"], 4)
     line = {
         "metric": "attention-backward TFLOP/s (bf16, causal) and % of MI355X dense MFMA peak",
         "value": round(tflops, 2),
@@ -328,22 +364,25 @@ def bench_workload(w, steps, warmup, with_cpu, inputs=None, mode="best"):
                    "parallelism": "single GPU"},
         "frac_of_peak": round(tflops / peak, 4),
         "mode": b.mode,
+        "plan": b.plan,
         "workspace_bytes": int(b.ws.numel()),
         "wall_ms_per_step": round(wall_ms, 4),
         "per_call_ms": calls,
         "caches": "L2 and MALL are not flushed between calls",
         "kernel_ms": {n: round(t, 4) for n, t in k_ms.items()},
+        "kernels": kernels,
         "preprocess_GBps": round(pre_bytes / (k_ms["preprocess"] * 1e-3) / 1e9, 1),
         "forward": {"ms": round(fwd_ms, 4), "tflops": round(fwd_tflops, 2),
                     "frac_of_peak": round(fwd_tflops / peak, 4)},
         "roofline": {
-            "kernel": dom,
+            "kernel": names[dom],
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": recorded_traffic(dom, w.name),
+            "traffic": recorded_traffic(names[dom], w.name),
+            "mfma_busy": recorded_value(names[dom], w.name, "counters", "mfma_busy_frac"),
             "flops_per_launch": kflops,
         },
         "cpu_baseline": cpu,

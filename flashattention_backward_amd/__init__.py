@@ -20,7 +20,7 @@ import math
 import os
 import threading
 
-__all__ = ["fwd", "bwd", "bwd_noalloc", "bwd_preprocess", "bwd_workspace_bytes", "lib", "FabError",
+__all__ = ["fwd", "bwd", "bwd_noalloc", "bwd_preprocess", "bwd_workspace_bytes", "bwd_plan", "lib", "FabError",
            "LIB_PATH", "DTYPE_CODES", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfab.so")
@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
             L.fab_bwd_workspace_bytes_min.argtypes = [i] * 7
             L.fab_bwd_workspace_bytes_ds.restype = sz
             L.fab_bwd_workspace_bytes_ds.argtypes = [i] * 7
+            L.fab_bwd_plan.restype = i
+            L.fab_bwd_plan.argtypes = [i] * 7 + [sz]
             L.fab_fwd.restype = i
             L.fab_fwd.argtypes = [vp] * 5 + [i] * 7 + [i, i, f, vp]
             L.fab_bwd_preprocess.restype = i
@@ -119,6 +121,17 @@ def bwd_workspace_bytes(B, H, H_kv, Sq, Sk, D, dtype_code, store_ds: bool | None
         if n:
             return n
     return int(L.fab_bwd_workspace_bytes_min(*args))
+
+
+PLANS = {0: "recompute", 1: "recompute_one_launch", 2: "stored_ds", 3: "f32"}
+
+
+def bwd_plan(B, H, H_kv, Sq, Sk, D, dtype_code, workspace_bytes) -> str:
+    """The launch sequence fab_bwd takes for these sizes and workspace size (see fab.h)."""
+    code = int(lib().fab_bwd_plan(B, H, H_kv, Sq, Sk, D, dtype_code, workspace_bytes))
+    if code < 0:
+        raise ValueError("invalid sizes or workspace too small")
+    return PLANS[code]
 
 
 def _window(window_size) -> int:

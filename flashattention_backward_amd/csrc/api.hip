@@ -370,6 +370,19 @@ size_t fab_bwd_workspace_bytes(int B, int H, int H_kv, int Sq, int Sk, int D, in
   return recommend_ds(B, H, H_kv, Sq, Sk, D, dtype) ? ws_bytes_ds(B, H, Sq, Sk) : ws_bytes(B, H, Sq);
 }
 
+int fab_bwd_plan(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype, size_t workspace_bytes) {
+  std::string saved = g_last_error;
+  fab_status s = check_common(B, H, H_kv, Sq, Sk, D, dtype);
+  g_last_error = saved;
+  if (s != FAB_OK || workspace_bytes < ws_bytes(B, H, Sq)) return -1;
+  if (!tiled(dtype)) return FAB_PLAN_F32;
+  if (use_ds(workspace_bytes, B, H, H_kv, Sq, Sk, dtype)) return FAB_PLAN_STORED_DS;
+  const fab::BwdParams p =
+      bwd_params(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                 B, H, H_kv, Sq, Sk, 0, 0, 1.f);
+  return fab::bwd_small16_fits(p, D) ? FAB_PLAN_RECOMPUTE_ONE_LAUNCH : FAB_PLAN_RECOMPUTE;
+}
+
 size_t fab_bwd_workspace_bytes_ds(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype) {
   std::string saved = g_last_error;
   fab_status s = check_common(B, H, H_kv, Sq, Sk, D, dtype);

@@ -105,6 +105,18 @@ size_t fab_bwd_workspace_bytes_min(int B, int H, int H_kv, int Sq, int Sk, int D
 size_t fab_bwd_workspace_bytes_ds(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype);
 
 /*
+ * The launches fab_bwd makes for these sizes and a workspace of `workspace_bytes` (-1 if the
+ * sizes are invalid or the workspace too small).  Enqueues nothing.
+ */
+typedef enum {
+  FAB_PLAN_RECOMPUTE = 0,             /* dQ kernel (step 1 in its prologue), then dK/dV     */
+  FAB_PLAN_RECOMPUTE_ONE_LAUNCH = 1,  /* step 1, then dQ and dK/dV kernels in one launch    */
+  FAB_PLAN_STORED_DS = 2,             /* step 1, dK/dV (also stores dS), dQ = scale dS K    */
+  FAB_PLAN_F32 = 3                    /* float32: step 1, dK/dV, dQ                         */
+} fab_plan;
+int fab_bwd_plan(int B, int H, int H_kv, int Sq, int Sk, int D, int dtype, size_t workspace_bytes);
+
+/*
  * Supporting forward (boostr autograd_attention.rs, var_flash_attention: the forward
  * returns the output and the lse that the backward consumes):
  *   o   = softmax(scale * q k^T over the allowed keys) v        [B, H, Sq, D], dtype

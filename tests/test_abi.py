@@ -54,6 +54,22 @@ def test_workspace_bytes():
     assert L.fab_bwd_workspace_bytes(1, 1, 1, 3, 5, 64, 9) == 0    # dtype
 
 
+def test_plan():
+    """The launch sequence follows the workspace size, the dtype and the problem size."""
+    L = fab.lib()
+    big = (2, 32, 8, 4096, 4096, 128, 2)
+    assert L.fab_bwd_plan(*big, L.fab_bwd_workspace_bytes_ds(*big)) == 2            # stored dS
+    assert L.fab_bwd_plan(*big, L.fab_bwd_workspace_bytes_min(*big)) == 0           # recompute
+    assert L.fab_bwd_plan(*big, L.fab_bwd_workspace_bytes(*big)) == 2               # recommended
+    small = (1, 8, 8, 1024, 1024, 64, 2)                                            # 64 + 64 workgroups
+    assert L.fab_bwd_plan(*small, L.fab_bwd_workspace_bytes(*small)) == 1
+    assert L.fab_bwd_plan(*small, L.fab_bwd_workspace_bytes_ds(*small)) == 2
+    assert L.fab_bwd_plan(1, 2, 2, 128, 128, 64, 0, 1 << 20) == 3                   # float32
+    assert L.fab_bwd_plan(*big, 16) == -1                                           # too small
+    assert L.fab_bwd_plan(1, 3, 2, 8, 8, 64, 2, 1 << 20) == -1                      # H % H_kv
+    assert fab.bwd_plan(*big, L.fab_bwd_workspace_bytes(*big)) == "stored_ds"
+
+
 P = 1 << 20  # a fake, 16-byte aligned address: validation must fail before using it
 
 
