@@ -37,6 +37,25 @@ def spans(S, W):
     return [(0, n), (mid, mid + n), (S - n - 11, S)]
 
 
+def compare_spans(tensors, S, W, scale, dt):
+    """Compare O, LSE, dQ on the exact rows and dK, dV on the exact keys of three spans
+    (start, middle, end) with the oracle run on each span's inputs."""
+    q, k, v, do, o, lse, dq, dk, dv = tensors
+    got = {key: [] for key in ("o", "lse", "dq", "dk", "dv")}
+    exp = {key: [] for key in got}
+    for c, e in spans(S, W):
+        rows, keys = window_span_ranges(c, e, S, W)
+        cut = lambda t: t[:, :, c:e].cpu()
+        ref = oracle.attention_grads(cut(q), cut(k), cut(v), cut(do), True, scale, window=W)
+        r0, r1 = rows[0] - c, rows[1] - c
+        k0, k1 = keys[0] - c, keys[1] - c
+        for key, t, a, b in (("o", o, r0, r1), ("lse", lse, r0, r1), ("dq", dq, r0, r1),
+                             ("dk", dk, k0, k1), ("dv", dv, k0, k1)):
+            got[key].append(to_np64(t[:, :, c + a:c + b]).ravel())
+            exp[key].append(np.asarray(ref[key])[:, :, a:b].ravel())
+    return got, exp
+
+
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
 def test_max_size_parity(fab, case):
     import torch
@@ -52,18 +71,35 @@ def test_max_size_parity(fab, case):
     dq, dk, dv = fab.bwd(do, q, k, v, o, lse, causal=True, scale=w.scale, window_size=W)
     torch.cuda.synchronize()
     say("    GPU forward and backward done")
-    got = {key: [] for key in ("o", "lse", "dq", "dk", "dv")}
-    exp = {key: [] for key in got}
-    for c, e in spans(S, W):
-        rows, keys = window_span_ranges(c, e, S, W)
-        cut = lambda t: t[:, :, c:e].cpu()
-        ref = oracle.attention_grads(cut(q), cut(k), cut(v), cut(do), True, w.scale, window=W)
-        r0, r1 = rows[0] - c, rows[1] - c
-        k0, k1 = keys[0] - c, keys[1] - c
-        for key, t, a, b in (("o", o, r0, r1), ("lse", lse, r0, r1), ("dq", dq, r0, r1),
-                             ("dk", dk, k0, k1), ("dv", dv, k0, k1)):
-            got[key].append(to_np64(t[:, :, c + a:c + b]).ravel())
-            exp[key].append(np.asarray(ref[key])[:, :, a:b].ravel())
+    got, exp = compare_spans((q, k, v, do, o, lse, dq, dk, dv), S, W, w.scale, dt)
+    del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    for key in got:
+        assert_close(key, np.concatenate(got[key]), np.concatenate(exp[key]),
+                     "fp32" if key == "lse" else dt)
+
+
+def test_stored_ds_largest_slab(fab):
+    """The stored-dS mode at the largest dS slab it takes: 2**31 bytes for one (batch, head)
+    (ragged Sq = Sk = 32731, rounded up to 32768 rows and keys), one query head per kv head, so
+    the group's dS buffer resource spans 2**31 bytes and the fragments near the slab's end sit
+    at 32-bit offsets just below it.  Spans of a causal sliding window are compared with the
+    oracle as in the maximum-size test."""
+    import torch
+    dt, H, H_kv, D, W = "bf16", 1, 1, 128, 192
+    S = 32768 - 37
+    code = fab.DTYPE_CODES["bfloat16"]
+    nb = fab.bwd_workspace_bytes(1, H, H_kv, S, S, D, code, store_ds=True)
+    assert nb > 2 ** 31 and fab.bwd_plan(1, H, H_kv, S, S, D, code, nb) == "stored_ds"
+    w = workloads.Workload("max_ds_slab", dt, 1, H, H_kv, S, S, D, True, seed=7301, window=W)
+    dev = torch.device("cuda:0")
+    say(f"[case] stored dS, largest slab: {dt} B=1 H={H} S={S} D={D} window={W}, workspace {nb} bytes")
+    q, k, v, do = workloads.make_inputs_device(w, dev)
+    o, lse = fab.fwd(q, k, v, causal=True, scale=w.scale, window_size=W)
+    dq, dk, dv = fab.bwd(do, q, k, v, o, lse, causal=True, scale=w.scale, window_size=W, store_ds=True)
+    torch.cuda.synchronize()
+    say("    GPU forward and backward done")
+    got, exp = compare_spans((q, k, v, do, o, lse, dq, dk, dv), S, W, w.scale, dt)
     del q, k, v, do, o, lse, dq, dk, dv
     torch.cuda.empty_cache()
     for key in got:
