@@ -48,6 +48,8 @@ SHAPES = [
     ("fp32", 1, 2, 1, 100, 150, 128, True),
     ("fp32", 2, 2, 2, 65, 33, 64, False),
     ("bf16", 1, 16, 2, 96, 96, 128, False),    # 8 query heads per kv head
+    ("bf16", 1, 6, 2, 300, 280, 128, True),    # 3 query heads per kv head (odd group)
+    ("fp16", 1, 5, 1, 140, 333, 96, False),    # 5 query heads per kv head, head dim 96
 ]
 
 
