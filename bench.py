@@ -277,6 +277,47 @@ def call_stats(ms):
             "p90": round(pct(0.9), 4)}
 
 
+PEAK_CLOCK_MHZ = 2400.0  # the clock the dense MFMA peaks assume (MI355X spec)
+
+
+def device_info():
+    """Name, architecture and compute units of cuda:0 as the runtime reports them."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count}
+
+
+def clock_under_load(fn, ms_target=60.0):
+    """Median shader clock (MHz) while `fn` runs back to back, outside the timed region:
+    about ms_target of calls are queued, then the current GFX clock is read (amdsmi, through
+    torch.cuda.clock_rate) until they have finished.  None where the clock cannot be read."""
+    import torch
+    try:
+        torch.cuda.clock_rate(0)
+    except Exception:
+        return None
+    t = time_launches(fn, 3, 1)
+    n = max(4, int(ms_target / max(t, 1e-3)))
+    done = torch.cuda.Event()
+    for _ in range(n):
+        fn()
+    done.record()
+    samples = []
+    while not done.query():
+        try:
+            c = float(torch.cuda.clock_rate(0))
+        except Exception:
+            break
+        if c > 0:
+            samples.append(c)
+        time.sleep(0.002)
+    torch.cuda.synchronize()
+    if not samples:
+        return None
+    samples.sort()
+    return samples[len(samples) // 2]
+
+
 def bench_workload(w, steps, warmup, with_cpu, inputs=None, mode="best"):
     import torch
     q, k, v, do = inputs if inputs is not None else workloads.make_inputs(w)
@@ -308,6 +349,8 @@ def bench_workload(w, steps, warmup, with_cpu, inputs=None, mode="best"):
     # the supporting forward, reported beside the metric (4 of the 10 counted units per pair);
     # it rewrites the same O and LSE, so the backward's inputs do not change
     fwd_ms = time_launches(b.fwd, steps, warmup)
+    # the clock the backward runs at (a separate loop, after everything timed above)
+    clk = clock_under_load(b.bwd)
     fwd_tflops = 0.4 * w.bwd_flops() / (fwd_ms * 1e-3) / 1e12
     flops = w.bwd_flops()
     tflops = flops / (ms * 1e-3) / 1e12
@@ -369,6 +412,9 @@ def bench_workload(w, steps, warmup, with_cpu, inputs=None, mode="best"):
         "wall_ms_per_step": round(wall_ms, 4),
         "per_call_ms": calls,
         "caches": "L2 and MALL are not flushed between calls",
+        "device": dict(device_info(), clock_mhz_under_load=clk,
+                       frac_of_peak_at_measured_clock=(round(tflops / (peak * clk / PEAK_CLOCK_MHZ), 4)
+                                                       if clk else None)),
         "kernel_ms": {n: round(t, 4) for n, t in k_ms.items()},
         "kernels": kernels,
         "preprocess_GBps": round(pre_bytes / (k_ms["preprocess"] * 1e-3) / 1e9, 1),
