@@ -29,12 +29,14 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("store_ds", [True, False], ids=["stored_ds", "recompute"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
-def test_window_parity(fab, case):
+def test_window_parity(fab, case, store_ds):
+    """Both modes (fp32 has one path, which either flag selects)."""
     dt, B, H, H_kv, Sq, Sk, D, causal, W = case
     w = workloads.Workload(f"win_{dt}", dt, B, H, H_kv, Sq, Sk, D, causal,
                            seed=3000 + Sq + 3 * Sk + W, window=W)
-    out, _ = check_end_to_end(fab, w)
+    out, _ = check_end_to_end(fab, w, store_ds=store_ds)
     if Sq - Sk >= W:  # rows without keys: exact zeros and -inf
         first = Sk + W - 1
         assert float(out["o"][:, :, first:].abs().max()) == 0.0
