@@ -26,12 +26,14 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("store_ds", [True, False], ids=["stored_ds", "recompute"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
-def test_head_dim_parity(fab, case):
+def test_head_dim_parity(fab, case, store_ds):
+    """Both modes (fp32 has one path, which either flag selects)."""
     dt, B, H, H_kv, Sq, Sk, D, causal, W = case
     w = workloads.Workload(f"hd{D}_{dt}", dt, B, H, H_kv, Sq, Sk, D, causal,
                            seed=5000 + D + Sq + W, window=W)
-    check_end_to_end(fab, w)
+    check_end_to_end(fab, w, store_ds=store_ds)
 
 
 def test_head_dim_256_isolated_backward(fab):
