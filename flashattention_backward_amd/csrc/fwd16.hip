@@ -144,7 +144,13 @@ __global__ __launch_bounds__(256, (HD <= 128 ? 2 : 1)) void fwd16_kernel(const F
     // n0 + 32 nb + 4 hl + off, off = 8 (r / 4) + r % 4, of row m; it is seen iff
     // kr.lo(m) <= key <= kr.hi(m).  Only steps that cut some row's keys test.
     const float c2 = p.scale_log2;
-    if (kr.hi(mw0) < n0 + BN - 1 || kr.lo(mw0 + 31) > n0) {
+    // On steps that cut some row's keys the scores are scaled here and the cut ones set to
+    // -inf.  Elsewhere the scale is applied inside the exponent's fma below (one vector
+    // instruction per score fewer): the row maximum of the scaled scores is then c2 times the
+    // maximum of the raw ones, or times their minimum when c2 < 0.
+    const bool cut = kr.hi(mw0) < n0 + BN - 1 || kr.lo(mw0 + 31) > n0;
+    float mx;
+    if (cut) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const int base = n0 + 32 * nb + 4 * hl;
@@ -155,17 +161,26 @@ __global__ __launch_bounds__(256, (HD <= 128 ? 2 : 1)) void fwd16_kernel(const F
           St[nb][r] = (off >= a && off <= z) ? St[nb][r] * c2 : -__builtin_inff();
         }
       }
-    } else {
+      mx = -__builtin_inff();
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) St[nb][r] *= c2;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, St[nb][r]);
+    } else if (c2 >= 0.f) {
+      float hi = -__builtin_inff();
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) hi = fmaxf(hi, St[nb][r]);
+      mx = hi * c2;
+    } else {
+      float lo = __builtin_inff();
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) lo = fminf(lo, St[nb][r]);
+      mx = lo * c2;
     }
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, St[nb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     // ---- lazy rescale (wave-uniform decision): only when some row's maximum grew by more
     // than kLazy; rows whose maximum did not grow get alpha = 1.
@@ -180,11 +195,12 @@ __global__ __launch_bounds__(256, (HD <= 128 ? 2 : 1)) void fwd16_kernel(const F
     // ---- P = exp2(score - mrun) <= 2^kLazy, its row sum, and its 16-bit fragments
     // (fragment (nb, ks): registers 8 ks .. 8 ks + 7 of block nb), the B operand of O^T.
     F pb[2][2];
+    const float sc = cut ? 1.f : c2;  // the scores' remaining scale factor
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pv = fast_exp2(St[nb][r] - mrun);
+        const float pv = fast_exp2(St[nb][r] * sc - mrun);
         lsum += pv;
         pb[nb][r >> 3][r & 7] = (T)pv;
       }
